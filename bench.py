@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark: one context-parallel rank's sparse-attention step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM:
+
+  prefill: cp_split_metadata (+ row gather of the input token ids),
+           kv_rerange of the latent KV and of the indexer keys,
+           indexer scores + top-k, sparse MLA (prefill kernel);
+  decode:  indexer scores + top-k on the paged pool, sparse MLA (decode).
+
+The step is timed end to end (K steps between two device synchronisations)
+and per call with HIP events on the stream the library launches on.  The
+printed JSON carries the roofline of the dominant kernel and the CPU
+oracle's rate on a bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "query tokens/s per GPU (indexer+top-k+sparse MLA); % of MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_t8000_cp8")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    return ap.parse_args()
+
+
+class Timed:
+    """HIP-event timing of named calls on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.events = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.events.setdefault(name, []).append((s, e))
+
+    def avg_ms(self):
+        return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.events.items()}
+
+
+def setup_prefill(wl, torch, ds, dev):
+    import numpy as np
+    from synth import draw_prefill
+
+    T, cp, r = wl.num_tokens, wl.cp_size, wl.cp_rank
+    n = ds.cp_local_count(T, cp, r)
+    inp = draw_prefill(wl, n)
+
+    def up(arr, fmt):
+        if fmt == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+        if fmt == "fp8":
+            return torch.from_numpy(arr).to(dev).view(torch.float8_e4m3fn)
+        return torch.from_numpy(arr).to(dev)
+
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    ids = torch.from_numpy(inp["input_ids"]).to(dev)
+    kv_l, ki_l = up(inp["kv"], wl.kv_fmt), up(inp["k_idx"], wl.kv_fmt)
+    slot = ds.cp_local_count(T, cp, 0)
+    # all-gather stand-in: every rank's own rows, rank after rank (built once
+    # by the split kernel, outside the timed region)
+    kv_cat = torch.empty((cp * slot, wl.d_qk), dtype=kv_l.dtype, device=dev)
+    ki_cat = torch.empty((cp * slot, wl.d_idx), dtype=ki_l.dtype, device=dev)
+    kv_cat.view(torch.uint8).fill_(0xFF)
+    ki_cat.view(torch.uint8).fill_(0xFF)
+    for rk in range(cp):
+        m = ds.cp_local_count(T, cp, rk)
+        if m:
+            ds.cp_split_metadata(cu, T, cp, rk, rows_src=kv_l, out={"rows": kv_cat[rk * slot: rk * slot + m]})
+            ds.cp_split_metadata(cu, T, cp, rk, rows_src=ki_l, out={"rows": ki_cat[rk * slot: rk * slot + m]})
+    del kv_l, ki_l
+    st = {
+        "n": n, "inp": inp, "cu": cu, "ids": ids, "kv_cat": kv_cat, "ki_cat": ki_cat,
+        "slot": slot,
+        "q_idx": up(inp["q_idx"], wl.act_fmt), "w": torch.from_numpy(inp["w"]).to(dev),
+        "q": up(inp["q"], wl.act_fmt),
+        "kv_scale": None if inp["kv_scale"] is None else torch.from_numpy(inp["kv_scale"]).to(dev),
+        "ki_scale": None if inp["k_idx_scale"] is None else torch.from_numpy(inp["k_idx_scale"]).to(dev),
+    }
+    i32 = dict(dtype=torch.int32, device=dev)
+    B = cu.numel() - 1
+    st["meta"] = {"local_cu": torch.empty(B + 1, **i32), "batch_idx": torch.empty(n, **i32),
+                  "global_idx": torch.empty(n, **i32), "kv_start": torch.empty(n, **i32),
+                  "kv_len": torch.empty(n, **i32), "rows": torch.empty(n, **i32)}
+    st["kv"] = torch.empty((T, wl.d_qk), dtype=kv_cat.dtype, device=dev)
+    st["ki"] = torch.empty((T, wl.d_idx), dtype=ki_cat.dtype, device=dev)
+    st["max_len"] = T
+    st["scores"] = torch.empty((n, ((T + 63) // 64) * 64), dtype=torch.float32, device=dev)
+    st["topk_idx"] = torch.empty((n, wl.topk), **i32)
+    st["out"] = torch.empty((n, wl.n_heads, wl.d_latent), dtype=torch.bfloat16 if wl.act_fmt != "f32" else torch.float32, device=dev)
+    st["lse"] = torch.empty((n, wl.n_heads), dtype=torch.float32, device=dev)
+    return st
+
+
+def prefill_step(wl, ds, st, tm):
+    T, cp, r = wl.num_tokens, wl.cp_size, wl.cp_rank
+    m = st["meta"]
+    tm.run("cp_split_metadata", lambda: ds.cp_split_metadata(st["cu"], T, cp, r, rows_src=st["ids"], out=m))
+    tm.run("kv_rerange(latent)", lambda: ds.kv_rerange(st["kv_cat"], st["slot"], T, cp, out=st["kv"]))
+    tm.run("kv_rerange(indexer_k)", lambda: ds.kv_rerange(st["ki_cat"], st["slot"], T, cp, out=st["ki"]))
+    tm.run("indexer_scores", lambda: ds.indexer_scores(st["q_idx"], st["w"], st["ki"], m["kv_start"], m["kv_len"], st["max_len"], k_scale=st["ki_scale"], scores=st["scores"]))
+    tm.run("topk_select", lambda: ds.topk_select(st["scores"], m["kv_start"], m["kv_len"], st["max_len"], wl.topk, T, topk_idx=st["topk_idx"]))
+    tm.run("sparse_mla", lambda: ds.sparse_mla_prefill(st["q"], st["kv"], st["topk_idx"], wl.scale, wl.d_latent, kv_scale=st["kv_scale"], out=st["out"], lse=st["lse"]))
+
+
+def setup_decode(wl, torch, ds, dev):
+    import numpy as np
+    from synth import draw_decode
+
+    inp = draw_decode(wl)
+
+    def up(arr, fmt):
+        if fmt == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+        if fmt == "fp8":
+            return torch.from_numpy(arr).to(dev).view(torch.float8_e4m3fn)
+        return torch.from_numpy(arr).to(dev)
+
+    n = wl.n_req
+    lengths = torch.from_numpy(inp["lengths"]).to(dev)
+    max_len = int(inp["lengths"].max())
+    st = {"n": n, "inp": inp, "meta": ds.decode_metadata(lengths),
+          "table": torch.from_numpy(inp["page_table"]).to(dev),
+          "ki": up(inp["k_idx"], wl.kv_fmt), "kv": up(inp["kv"], wl.kv_fmt),
+          "q_idx": up(inp["q_idx"], wl.act_fmt), "w": torch.from_numpy(inp["w"]).to(dev),
+          "q": up(inp["q"], wl.act_fmt), "max_len": max_len,
+          "kv_scale": None if inp["kv_scale"] is None else torch.from_numpy(inp["kv_scale"]).to(dev),
+          "ki_scale": None if inp["k_idx_scale"] is None else torch.from_numpy(inp["k_idx_scale"]).to(dev)}
+    st["scores"] = torch.empty((n, ((max_len + 63) // 64) * 64), dtype=torch.float32, device=dev)
+    st["topk_idx"] = torch.empty((n, wl.topk), dtype=torch.int32, device=dev)
+    st["out"] = torch.empty((n, wl.n_heads, wl.d_latent), dtype=torch.bfloat16, device=dev)
+    st["lse"] = torch.empty((n, wl.n_heads), dtype=torch.float32, device=dev)
+    st["ws"] = torch.empty(ds.sparse_mla_workspace_size(n, wl.n_heads, wl.d_latent, wl.topk),
+                           dtype=torch.uint8, device=dev)
+    return st
+
+
+def decode_step(wl, ds, st, tm):
+    m = st["meta"]
+    paging = dict(q_req=m["q_req"], page_table=st["table"], page_size=wl.page_size)
+    k_rows = st["ki"].shape[0]
+    tm.run("indexer_scores", lambda: ds.indexer_scores(st["q_idx"], st["w"], st["ki"], m["kv_start"], m["kv_len"], st["max_len"], k_scale=st["ki_scale"], scores=st["scores"], **paging))
+    tm.run("topk_select", lambda: ds.topk_select(st["scores"], m["kv_start"], m["kv_len"], st["max_len"], wl.topk, k_rows, topk_idx=st["topk_idx"], **paging))
+    tm.run("sparse_mla", lambda: ds.sparse_mla_decode(st["q"], st["kv"], st["topk_idx"], wl.scale, wl.d_latent, kv_scale=st["kv_scale"], out=st["out"], lse=st["lse"], workspace=st["ws"]))
+
+
+def work_model(wl, kv_len):
+    """Algorithmic work per call: causal pairs for the indexer, valid top-k
+    pairs for MLA; bytes are the unavoidable HBM traffic of each call."""
+    import numpy as np
+    kv_len = np.asarray(kv_len, dtype=np.int64)
+    n = kv_len.size
+    idx_pairs = int(kv_len.sum())
+    mla_pairs = int(np.minimum(kv_len, wl.topk).sum())
+    act = 4 if wl.act_fmt == "f32" else 2
+    kvb = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_fmt]
+    T = wl.num_tokens if wl.kind == "prefill" else 0
+    mla_flops = mla_pairs * 2 * wl.n_heads * (2 * wl.d_latent + wl.d_rope)
+    idx_flops = idx_pairs * (2 * wl.h_idx * wl.d_idx + wl.h_idx)
+    out = {
+        "indexer_scores": {"flops": idx_flops,
+                           "bytes": n * wl.h_idx * (wl.d_idx * act + 4)
+                           + (T if T else idx_pairs) * wl.d_idx * kvb + idx_pairs * 4},
+        "topk_select": {"flops": 0, "bytes": idx_pairs * 4 + n * wl.topk * 4},
+        "sparse_mla": {"flops": mla_flops,
+                       "bytes": n * wl.n_heads * (wl.d_qk * act + wl.d_latent * 2 + 4)
+                       + mla_pairs * wl.d_qk * kvb + n * wl.topk * 4},
+    }
+    if wl.kind == "prefill":
+        row = lambda d: d * kvb  # noqa: E731
+        out["kv_rerange(latent)"] = {"flops": 0, "bytes": 2 * T * row(wl.d_qk)}
+        out["kv_rerange(indexer_k)"] = {"flops": 0, "bytes": 2 * T * row(wl.d_idx)}
+        out["cp_split_metadata"] = {"flops": 0, "bytes": n * 4 * 6}
+    return out, idx_pairs, mla_pairs
+
+
+def cpu_baseline(wl, st, kv_len_host, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of query rows."""
+    import numpy as np
+    from oracle import pipeline as opl
+    from oracle import round_robin_cp as orr
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    inp = st["inp"]
+    n = st["n"]
+    if wl.kind == "prefill":
+        meta = orr.split_metadata(inp["cu_seqlens"], wl.cp_size, wl.cp_rank)
+        paging = {}
+    else:
+        meta = opl.decode_metadata(inp["lengths"])
+        paging = {"page_table": inp["page_table"], "page_size": wl.page_size}
+    order = np.linspace(0, n - 1, num=min(n, 64)).astype(int)
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    done, t0 = 0, time.perf_counter()
+    for j in order:
+        sel = opl.indexer_topk_rows([j], meta, inp["q_idx"], wl.act_fmt, inp["w"], inp["k_idx"],
+                                    wl.kv_fmt, inp["k_idx_scale"], wl.topk, **paging)
+        opl.sparse_mla_rows([j], [sel[0]["topk_idx"]], inp["q"], wl.act_fmt, inp["kv"],
+                            wl.kv_fmt, inp["kv_scale"], wl.scale, wl.d_latent)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "query tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} of {n} query rows (evenly spaced over the rank's queries, "
+                      f"shuffled), indexer + top-k + sparse MLA in float64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this build runs one context-parallel rank on one GPU; "
+              f"--gpus {args.gpus} is not supported (multi-GPU sharding is design-only).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import deepseek_v3_context_amd as ds
+    from synth import get
+
+    wl = get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] setting up {wl.name}", file=sys.stderr, flush=True)
+    if wl.kind == "prefill":
+        st = setup_prefill(wl, torch, ds, dev)
+        step = prefill_step
+    else:
+        st = setup_decode(wl, torch, ds, dev)
+        step = decode_step
+    torch.cuda.synchronize()
+
+    warm = Timed(torch)
+    for _ in range(args.warmup):
+        step(wl, ds, st, warm)
+    torch.cuda.synchronize()
+    if wl.kind == "prefill":
+        kv_len_host = st["meta"]["kv_len"].cpu().numpy()
+    else:
+        kv_len_host = st["inp"]["lengths"]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    tm = Timed(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(wl, ds, st, tm)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_call = tm.avg_ms()
+    model, idx_pairs, mla_pairs = work_model(wl, kv_len_host)
+    kernels = {}
+    for name, ms in per_call.items():
+        w = model.get(name, {"flops": 0, "bytes": 0})
+        kernels[name] = {"avg_us": round(ms * 1e3, 2),
+                         "tflops": round(w["flops"] / (ms * 1e-3) / 1e12, 2),
+                         "gbs": round(w["bytes"] / (ms * 1e-3) / 1e9, 1)}
+    dom = max(per_call, key=per_call.get)
+    dw = model[dom]
+    d_ms = per_call[dom]
+    if dw["flops"] and dw["flops"] / max(dw["bytes"], 1) > 315:
+        ach = dw["flops"] / (d_ms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+    else:
+        ach = dw["bytes"] / (d_ms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": None}
+    n = st["n"]
+    ms_step = elapsed / args.steps * 1e3
+    line = {
+        "metric": METRIC, "value": round(n * args.steps / elapsed, 1),
+        "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if wl.act_fmt == "bf16" else wl.act_fmt,
+        "data": "synthetic (seeded N(0,1)/sqrt(dim) activations; no trained weights)",
+        "config": {"workload": wl.name, "kind": wl.kind, "queries": n,
+                   "num_tokens": wl.num_tokens if wl.kind == "prefill" else int(np.sum(kv_len_host)),
+                   "cp_size": wl.cp_size, "cp_rank": wl.cp_rank, "topk": wl.topk,
+                   "heads": wl.n_heads, "d_latent": wl.d_latent, "d_rope": wl.d_rope,
+                   "indexer": f"{wl.h_idx}x{wl.d_idx}", "kv_format": wl.kv_fmt,
+                   "indexer_pairs": idx_pairs, "mla_pairs": mla_pairs},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, st, kv_len_host, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,290 @@
+"""ctypes binding of libds32cp.so (the C ABI in include/ds32cp.h).
+
+Argument marshalling only: tensors are passed as device pointers with their
+sizes, the stream is torch's current HIP stream, and every compute step
+runs in the HIP library.  Output buffers may be passed in (nothing is
+allocated then) or are allocated here with torch as plain device memory.
+There is no fallback: if the library is missing, importing this module
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("DS32CP_LIB", os.path.join(_HERE, "libds32cp.so"))
+
+DS_F32, DS_BF16, DS_FP8_E4M3FN = 0, 1, 2
+STATUS = {0: "DS_OK", 1: "DS_ERR_INVALID_ARG", 2: "DS_ERR_UNSUPPORTED",
+          3: "DS_ERR_WORKSPACE", 4: "DS_ERR_HIP"}
+
+
+class DS32CPError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"ds32cp HIP library not found at {LIB_PATH}; build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'`")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_p, _i32, _i64, _sz, _f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                             ctypes.c_size_t, ctypes.c_float)
+_SIGS = {
+    "ds_abi_version": ([], _i32),
+    "ds_last_error": ([], ctypes.c_char_p),
+    "ds_cp_local_count": ([_i64, _i32, _i32], _i32),
+    "cp_split_metadata": ([_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
+                           _i64, _p], _i32),
+    "kv_rerange": ([_p, _i32, _i32, _i32, _i64, _p, _p], _i32),
+    "indexer_topk_workspace_size": ([_i32, _i32], _sz),
+    "indexer_topk": ([_p, _i32, _p, _p, _i32, _p, _i64, _p, _p, _p, _p, _i32, _i32,
+                      _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _sz, _p], _i32),
+    "indexer_scores": ([_p, _i32, _p, _p, _i32, _p, _i64, _p, _p, _p, _p, _i32, _i32,
+                        _i32, _i32, _i32, _i32, _i32, _p, _i64, _p], _i32),
+    "topk_select": ([_p, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i64, _i32, _i32,
+                     _i32, _p, _p, _p], _i32),
+    "sparse_mla_prefill": ([_p, _i32, _p, _i32, _p, _i64, _p, _i32, _i32, _i32, _i32,
+                            _i32, _f32, _p, _i32, _p, _p], _i32),
+    "sparse_mla_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
+    "sparse_mla_decode": ([_p, _i32, _p, _i32, _p, _i64, _p, _i32, _i32, _i32, _i32,
+                           _i32, _f32, _p, _i32, _p, _p, _sz, _p], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise DS32CPError(fn, status, lib.ds_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a torch tensor, got {type(t).__name__}")
+    if t.numel() and not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DS_F32
+    if t.dtype == torch.bfloat16:
+        return DS_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return DS_FP8_E4M3FN
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _i32buf(n, device, out):
+    if out is not None:
+        return out
+    return torch.empty(max(n, 0), dtype=torch.int32, device=device)
+
+
+# --------------------------------------------------------------------- api
+
+def abi_version() -> int:
+    return lib.ds_abi_version()
+
+
+def cp_local_count(num_tokens: int, cp_size: int, cp_rank: int) -> int:
+    n = lib.ds_cp_local_count(num_tokens, cp_size, cp_rank)
+    if n < 0:
+        raise ValueError("invalid cp_size / cp_rank / num_tokens")
+    return n
+
+
+def cp_split_metadata(cu_seqlens: torch.Tensor, num_tokens: int, cp_size: int,
+                      cp_rank: int, rows_src: torch.Tensor | None = None,
+                      out: dict | None = None, stream=None) -> dict:
+    """Step 1.  Returns dict with local_cu, batch_idx, global_idx, kv_start,
+    kv_len (and rows when rows_src is given)."""
+    dev = cu_seqlens.device
+    B = cu_seqlens.numel() - 1
+    n = cp_local_count(num_tokens, cp_size, cp_rank)
+    out = dict(out or {})
+    res = {
+        "local_cu": _i32buf(B + 1, dev, out.get("local_cu")),
+        "batch_idx": _i32buf(n, dev, out.get("batch_idx")),
+        "global_idx": _i32buf(n, dev, out.get("global_idx")),
+        "kv_start": _i32buf(n, dev, out.get("kv_start")),
+        "kv_len": _i32buf(n, dev, out.get("kv_len")),
+    }
+    row_bytes = 0
+    if rows_src is not None:
+        row_bytes = rows_src.element_size() * math.prod(rows_src.shape[1:])
+        rows = out.get("rows")
+        if rows is None:
+            rows = torch.empty((n,) + tuple(rows_src.shape[1:]), dtype=rows_src.dtype, device=dev)
+        res["rows"] = rows
+    st = lib.cp_split_metadata(
+        _ptr(cu_seqlens), B, num_tokens, cp_size, cp_rank, _ptr(res["local_cu"]),
+        _ptr(res["batch_idx"]), _ptr(res["global_idx"]), _ptr(res["kv_start"]),
+        _ptr(res["kv_len"]), _ptr(rows_src), _ptr(res.get("rows")), row_bytes,
+        _stream(stream))
+    _check("cp_split_metadata", st)
+    return res
+
+
+def kv_rerange(src: torch.Tensor, slot_rows: int, num_tokens: int, cp_size: int,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Step 2: rank-concatenated rows -> logical order (row = first axis)."""
+    row_bytes = src.element_size() * math.prod(src.shape[1:])
+    if out is None:
+        out = torch.empty((num_tokens,) + tuple(src.shape[1:]), dtype=src.dtype,
+                          device=src.device)
+    st = lib.kv_rerange(_ptr(src), slot_rows, num_tokens, cp_size, row_bytes, _ptr(out),
+                        _stream(stream))
+    _check("kv_rerange", st)
+    return out
+
+
+def indexer_topk_workspace_size(n_q: int, max_kv_len: int) -> int:
+    return lib.indexer_topk_workspace_size(n_q, max_kv_len)
+
+
+def _paging(q_req, page_table, page_size):
+    if page_table is None:
+        return None, None, 0, 0, 0
+    return (_ptr(q_req), _ptr(page_table), page_table.shape[0], page_size,
+            page_table.shape[1])
+
+
+def indexer_topk(q_idx, w, k_idx, kv_start, kv_len, max_kv_len: int, topk: int,
+                 k_scale=None, q_req=None, page_table=None, page_size: int = 0,
+                 topk_idx=None, topk_score=None, want_score: bool = False,
+                 workspace=None, stream=None):
+    """Steps 3 + 4.  Returns (topk_idx [n_q, topk] int32, topk_score or None)."""
+    n_q, h_idx, d_idx = q_idx.shape
+    dev = q_idx.device
+    if topk_idx is None:
+        topk_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
+    if want_score and topk_score is None:
+        topk_score = torch.empty((n_q, topk), dtype=torch.float32, device=dev)
+    ws_bytes = indexer_topk_workspace_size(n_q, max_kv_len)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    qr, pt, n_req, ps, mp = _paging(q_req, page_table, page_size)
+    st = lib.indexer_topk(
+        _ptr(q_idx), dtype_code(q_idx), _ptr(w), _ptr(k_idx), dtype_code(k_idx),
+        _ptr(k_scale), k_idx.shape[0], _ptr(kv_start), _ptr(kv_len), qr, pt, n_req, ps, mp,
+        n_q, h_idx, d_idx, max_kv_len, topk, _ptr(topk_idx), _ptr(topk_score),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("indexer_topk", st)
+    return topk_idx, topk_score
+
+
+def indexer_scores(q_idx, w, k_idx, kv_start, kv_len, max_kv_len: int, k_scale=None,
+                   q_req=None, page_table=None, page_size: int = 0, scores=None,
+                   stream=None) -> torch.Tensor:
+    """Step 3 alone: scores [n_q, max_kv_len] fp32 (entries past kv_len are
+    left as allocated: NaN when allocated here)."""
+    n_q, h_idx, d_idx = q_idx.shape
+    if scores is None:
+        scores = torch.full((n_q, max(max_kv_len, 1)), float("nan"), dtype=torch.float32,
+                            device=q_idx.device)
+    qr, pt, n_req, ps, mp = _paging(q_req, page_table, page_size)
+    st = lib.indexer_scores(
+        _ptr(q_idx), dtype_code(q_idx), _ptr(w), _ptr(k_idx), dtype_code(k_idx),
+        _ptr(k_scale), k_idx.shape[0], _ptr(kv_start), _ptr(kv_len), qr, pt, n_req, ps, mp,
+        n_q, h_idx, d_idx, max_kv_len, _ptr(scores), scores.shape[1], _stream(stream))
+    _check("indexer_scores", st)
+    return scores
+
+
+def topk_select(scores, kv_start, kv_len, max_kv_len: int, topk: int, k_rows: int,
+                q_req=None, page_table=None, page_size: int = 0, topk_idx=None,
+                topk_score=None, want_score: bool = False, stream=None):
+    n_q = scores.shape[0]
+    dev = scores.device
+    if topk_idx is None:
+        topk_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
+    if want_score and topk_score is None:
+        topk_score = torch.empty((n_q, topk), dtype=torch.float32, device=dev)
+    qr, pt, n_req, ps, mp = _paging(q_req, page_table, page_size)
+    st = lib.topk_select(_ptr(scores), scores.shape[1], _ptr(kv_start), _ptr(kv_len), qr, pt,
+                         n_req, ps, mp, k_rows, n_q, max_kv_len, topk, _ptr(topk_idx),
+                         _ptr(topk_score), _stream(stream))
+    _check("topk_select", st)
+    return topk_idx, topk_score
+
+
+def _mla_common(q, kv, topk_idx, d_latent, out, out_dtype):
+    n_q, n_heads, d_qk = q.shape
+    if out is None:
+        out = torch.empty((n_q, n_heads, d_latent), dtype=out_dtype, device=q.device)
+    return n_q, n_heads, d_qk - d_latent, out
+
+
+def sparse_mla_prefill(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale=None,
+                       out=None, out_dtype=None, lse=None, want_lse: bool = True,
+                       stream=None):
+    """Step 5 (prefill).  Returns (out [n_q, H, d_latent], lse [n_q, H] or None)."""
+    out_dtype = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
+    n_q, H, d_rope, out = _mla_common(q, kv, topk_idx, d_latent, out, out_dtype)
+    if want_lse and lse is None:
+        lse = torch.empty((n_q, H), dtype=torch.float32, device=q.device)
+    st = lib.sparse_mla_prefill(
+        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv), _ptr(kv_scale), kv.shape[0],
+        _ptr(topk_idx), n_q, H, d_latent, d_rope, topk_idx.shape[1], sm_scale, _ptr(out),
+        dtype_code(out), _ptr(lse), _stream(stream))
+    _check("sparse_mla_prefill", st)
+    return out, lse
+
+
+def sparse_mla_workspace_size(n_q: int, n_heads: int, d_latent: int, topk: int) -> int:
+    return lib.sparse_mla_workspace_size(n_q, n_heads, d_latent, topk)
+
+
+def sparse_mla_decode(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale=None,
+                      out=None, out_dtype=None, lse=None, want_lse: bool = True,
+                      workspace=None, stream=None):
+    """Step 5 (decode: rows split across workgroups, merged by LSE)."""
+    out_dtype = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
+    n_q, H, d_rope, out = _mla_common(q, kv, topk_idx, d_latent, out, out_dtype)
+    if want_lse and lse is None:
+        lse = torch.empty((n_q, H), dtype=torch.float32, device=q.device)
+    topk = topk_idx.shape[1]
+    ws_bytes = sparse_mla_workspace_size(n_q, H, d_latent, topk)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = lib.sparse_mla_decode(
+        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv), _ptr(kv_scale), kv.shape[0],
+        _ptr(topk_idx), n_q, H, d_latent, d_rope, topk, sm_scale, _ptr(out), dtype_code(out),
+        _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("sparse_mla_decode", st)
+    return out, lse
+
+
+def decode_metadata(lengths: torch.Tensor) -> dict:
+    """Decode step metadata: request i has one query whose causal keys are
+    positions 0 .. L_i - 1 of that request (its own KV already cached)."""
+    n = lengths.numel()
+    dev = lengths.device
+    return {"q_req": torch.arange(n, dtype=torch.int32, device=dev),
+            "kv_start": torch.zeros(n, dtype=torch.int32, device=dev),
+            "kv_len": lengths.to(torch.int32).contiguous()}

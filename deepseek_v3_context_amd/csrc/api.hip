@@ -1,0 +1,273 @@
+// Host side of the C ABI declared in include/ds32cp.h: argument checks
+// (before any launch), workspace sizing and dispatch to the kernels.
+#include <stdio.h>
+
+#include <string>
+
+#include "common.h"
+
+namespace ds32cp {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+ds_status fail(ds_status code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+ds_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(DS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return DS_OK;
+}
+
+static bool is_act_dtype(ds_dtype d) { return d == DS_F32 || d == DS_BF16; }
+
+}  // namespace ds32cp
+
+using namespace ds32cp;
+
+#define DS_REQUIRE(cond, code, msg) \
+  do {                              \
+    if (!(cond)) return fail((code), (msg)); \
+  } while (0)
+
+extern "C" {
+
+int32_t ds_abi_version(void) { return 1; }
+
+const char* ds_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ds_cp_local_count(int64_t num_tokens, int32_t cp_size, int32_t cp_rank) {
+  if (cp_size < 1 || cp_rank < 0 || cp_rank >= cp_size || num_tokens < 0) return -1;
+  if (num_tokens <= cp_rank) return 0;
+  const int64_t n = (num_tokens - cp_rank + cp_size - 1) / cp_size;
+  return n > INT32_MAX ? -1 : static_cast<int32_t>(n);
+}
+
+ds_status cp_split_metadata(const int32_t* cu_seqlens, int32_t num_reqs,
+                            int32_t num_tokens, int32_t cp_size, int32_t cp_rank,
+                            int32_t* local_cu, int32_t* batch_idx,
+                            int32_t* global_idx, int32_t* kv_start,
+                            int32_t* kv_len, const void* rows_src, void* rows_dst,
+                            int64_t row_bytes, hipStream_t stream) {
+  DS_REQUIRE(cp_size >= 1, DS_ERR_INVALID_ARG, "cp_split_metadata: cp_size must be >= 1");
+  DS_REQUIRE(cp_rank >= 0 && cp_rank < cp_size, DS_ERR_INVALID_ARG,
+             "cp_split_metadata: cp_rank outside [0, cp_size)");
+  DS_REQUIRE(num_tokens >= 0, DS_ERR_INVALID_ARG, "cp_split_metadata: num_tokens < 0");
+  DS_REQUIRE(num_reqs >= 1, DS_ERR_INVALID_ARG, "cp_split_metadata: num_reqs must be >= 1");
+  DS_REQUIRE(cu_seqlens != nullptr, DS_ERR_INVALID_ARG, "cp_split_metadata: cu_seqlens is NULL");
+  DS_REQUIRE(rows_src == nullptr || (rows_dst != nullptr && row_bytes > 0),
+             DS_ERR_INVALID_ARG,
+             "cp_split_metadata: row gather needs rows_dst and row_bytes > 0");
+  const int32_t n = ds_cp_local_count(num_tokens, cp_size, cp_rank);
+  ds_status st = launch_split_metadata(cu_seqlens, num_reqs, num_tokens, cp_size, cp_rank,
+                                       n, local_cu, batch_idx, global_idx, kv_start,
+                                       kv_len, stream);
+  if (st != DS_OK || rows_src == nullptr) return st;
+  return launch_row_gather_rr(rows_src, rows_dst, n, cp_size, cp_rank, row_bytes, stream);
+}
+
+ds_status kv_rerange(const void* src, int32_t slot_rows, int32_t num_tokens,
+                     int32_t cp_size, int64_t row_bytes, void* dst,
+                     hipStream_t stream) {
+  DS_REQUIRE(cp_size >= 1, DS_ERR_INVALID_ARG, "kv_rerange: cp_size must be >= 1");
+  DS_REQUIRE(num_tokens >= 0, DS_ERR_INVALID_ARG, "kv_rerange: num_tokens < 0");
+  DS_REQUIRE(row_bytes > 0, DS_ERR_INVALID_ARG, "kv_rerange: row_bytes must be > 0");
+  DS_REQUIRE(static_cast<int64_t>(slot_rows) * cp_size >= num_tokens && slot_rows >= 0,
+             DS_ERR_INVALID_ARG, "kv_rerange: slot_rows < ceil(num_tokens / cp_size)");
+  DS_REQUIRE(num_tokens == 0 || (src != nullptr && dst != nullptr), DS_ERR_INVALID_ARG,
+             "kv_rerange: NULL buffer");
+  if (num_tokens > 0) {
+    const char* s0 = static_cast<const char*>(src);
+    const char* d0 = static_cast<const char*>(dst);
+    const int64_t sb = static_cast<int64_t>(slot_rows) * cp_size * row_bytes;
+    const int64_t db = static_cast<int64_t>(num_tokens) * row_bytes;
+    DS_REQUIRE(s0 + sb <= d0 || d0 + db <= s0, DS_ERR_INVALID_ARG,
+               "kv_rerange: src and dst overlap");
+  }
+  return launch_rerange(src, dst, num_tokens, cp_size, slot_rows, row_bytes, stream);
+}
+
+static ds_status check_indexer(const char* fn, const IndexerArgs& a) {
+  const std::string f(fn);
+  DS_REQUIRE(a.n_q >= 0 && a.max_kv_len >= 0 && a.k_rows >= 0, DS_ERR_INVALID_ARG,
+             f + ": negative size");
+  DS_REQUIRE(a.h_idx >= 1 && a.d_idx >= 1, DS_ERR_INVALID_ARG, f + ": h_idx/d_idx must be >= 1");
+  if (a.n_q > 0) {
+    DS_REQUIRE(a.q_idx && a.w && a.kv_start && a.kv_len, DS_ERR_INVALID_ARG,
+               f + ": NULL query/weight/metadata pointer");
+    DS_REQUIRE(a.k_rows == 0 || a.k_idx, DS_ERR_INVALID_ARG, f + ": NULL key pointer");
+  }
+  DS_REQUIRE(is_act_dtype(a.q_dtype), DS_ERR_UNSUPPORTED, f + ": q_idx must be f32 or bf16");
+  if (a.page_table != nullptr) {
+    DS_REQUIRE(a.q_req != nullptr, DS_ERR_INVALID_ARG, f + ": paged keys need q_req");
+    DS_REQUIRE(a.page_size >= 1 && a.max_pages >= 1 && a.n_req >= 1, DS_ERR_INVALID_ARG,
+               f + ": page_size, max_pages and n_req must be >= 1");
+  }
+  if (a.q_dtype == DS_F32) {
+    DS_REQUIRE(a.k_dtype == DS_F32 || a.k_dtype == DS_BF16, DS_ERR_UNSUPPORTED,
+               f + ": f32 queries need f32 or bf16 keys");
+    DS_REQUIRE(a.h_idx <= 64 && a.d_idx <= 128, DS_ERR_UNSUPPORTED,
+               f + ": f32 path supports h_idx <= 64, d_idx <= 128");
+  } else {
+    DS_REQUIRE(a.k_dtype == DS_BF16 || a.k_dtype == DS_FP8_E4M3FN, DS_ERR_UNSUPPORTED,
+               f + ": bf16 queries need bf16 or fp8 keys");
+    DS_REQUIRE(a.h_idx == 64 && a.d_idx == 128, DS_ERR_UNSUPPORTED,
+               f + ": bf16 path supports h_idx == 64, d_idx == 128");
+  }
+  if (a.k_dtype == DS_FP8_E4M3FN)
+    DS_REQUIRE(a.k_scale != nullptr, DS_ERR_INVALID_ARG, f + ": fp8 keys need k_scale");
+  return DS_OK;
+}
+
+size_t indexer_topk_workspace_size(int32_t n_q, int32_t max_kv_len) {
+  if (n_q <= 0 || max_kv_len <= 0) return 256;
+  return sizeof(float) * static_cast<size_t>(n_q) * static_cast<size_t>(round_up(max_kv_len, 64));
+}
+
+ds_status indexer_scores(const void* q_idx, ds_dtype q_dtype, const float* w,
+                         const void* k_idx, ds_dtype k_dtype, const float* k_scale,
+                         int64_t k_rows, const int32_t* kv_start, const int32_t* kv_len,
+                         const int32_t* q_req, const int32_t* page_table, int32_t n_req,
+                         int32_t page_size, int32_t max_pages, int32_t n_q, int32_t h_idx,
+                         int32_t d_idx, int32_t max_kv_len, float* scores,
+                         int64_t score_stride, hipStream_t stream) {
+  IndexerArgs a{q_idx, q_dtype, w, k_idx, k_dtype, k_scale, k_rows, kv_start, kv_len,
+                q_req, page_table, n_req, page_size, max_pages, n_q, h_idx, d_idx,
+                max_kv_len, scores, score_stride};
+  ds_status st = check_indexer("indexer_scores", a);
+  if (st != DS_OK) return st;
+  DS_REQUIRE(score_stride >= max_kv_len, DS_ERR_INVALID_ARG,
+             "indexer_scores: score_stride < max_kv_len");
+  DS_REQUIRE(n_q == 0 || scores != nullptr, DS_ERR_INVALID_ARG, "indexer_scores: NULL scores");
+  return launch_indexer_scores(a, stream);
+}
+
+static ds_status check_topk(const char* fn, int32_t n_q, int32_t topk, const int32_t* idx,
+                            const int32_t* kv_start, const int32_t* kv_len,
+                            const int32_t* q_req, const int32_t* page_table,
+                            int32_t n_req, int32_t page_size, int32_t max_pages) {
+  const std::string f(fn);
+  DS_REQUIRE(topk >= 1 && topk <= 2048, DS_ERR_INVALID_ARG, f + ": topk must be in [1, 2048]");
+  DS_REQUIRE(n_q == 0 || (idx && kv_start && kv_len), DS_ERR_INVALID_ARG,
+             f + ": NULL topk_idx or metadata");
+  if (page_table != nullptr)
+    DS_REQUIRE(q_req != nullptr && page_size >= 1 && max_pages >= 1 && n_req >= 1,
+               DS_ERR_INVALID_ARG, f + ": bad paging arguments");
+  return DS_OK;
+}
+
+ds_status topk_select(const float* scores, int64_t score_stride, const int32_t* kv_start,
+                      const int32_t* kv_len, const int32_t* q_req,
+                      const int32_t* page_table, int32_t n_req, int32_t page_size,
+                      int32_t max_pages, int64_t k_rows, int32_t n_q, int32_t max_kv_len,
+                      int32_t topk, int32_t* topk_idx, float* topk_score,
+                      hipStream_t stream) {
+  DS_REQUIRE(n_q >= 0 && max_kv_len >= 0 && k_rows >= 0, DS_ERR_INVALID_ARG,
+             "topk_select: negative size");
+  DS_REQUIRE(score_stride >= max_kv_len, DS_ERR_INVALID_ARG, "topk_select: score_stride < max_kv_len");
+  DS_REQUIRE(n_q == 0 || scores != nullptr, DS_ERR_INVALID_ARG, "topk_select: NULL scores");
+  ds_status st = check_topk("topk_select", n_q, topk, topk_idx, kv_start, kv_len, q_req,
+                            page_table, n_req, page_size, max_pages);
+  if (st != DS_OK) return st;
+  TopkArgs t{scores, score_stride, kv_start, kv_len, q_req, page_table, n_req, page_size,
+             max_pages, k_rows, n_q, max_kv_len, topk, topk_idx, topk_score};
+  return launch_topk(t, stream);
+}
+
+ds_status indexer_topk(const void* q_idx, ds_dtype q_dtype, const float* w,
+                       const void* k_idx, ds_dtype k_dtype, const float* k_scale,
+                       int64_t k_rows, const int32_t* kv_start, const int32_t* kv_len,
+                       const int32_t* q_req, const int32_t* page_table, int32_t n_req,
+                       int32_t page_size, int32_t max_pages, int32_t n_q, int32_t h_idx,
+                       int32_t d_idx, int32_t max_kv_len, int32_t topk,
+                       int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  const int64_t stride = round_up(max_kv_len > 0 ? max_kv_len : 1, 64);
+  IndexerArgs a{q_idx, q_dtype, w, k_idx, k_dtype, k_scale, k_rows, kv_start, kv_len,
+                q_req, page_table, n_req, page_size, max_pages, n_q, h_idx, d_idx,
+                max_kv_len, static_cast<float*>(ws), stride};
+  ds_status st = check_indexer("indexer_topk", a);
+  if (st != DS_OK) return st;
+  st = check_topk("indexer_topk", n_q, topk, topk_idx, kv_start, kv_len, q_req, page_table,
+                  n_req, page_size, max_pages);
+  if (st != DS_OK) return st;
+  DS_REQUIRE(ws != nullptr && ws_bytes >= indexer_topk_workspace_size(n_q, max_kv_len),
+             DS_ERR_WORKSPACE, "indexer_topk: workspace smaller than indexer_topk_workspace_size()");
+  st = launch_indexer_scores(a, stream);
+  if (st != DS_OK) return st;
+  TopkArgs t{static_cast<const float*>(ws), stride, kv_start, kv_len, q_req, page_table,
+             n_req, page_size, max_pages, k_rows, n_q, max_kv_len, topk, topk_idx, topk_score};
+  return launch_topk(t, stream);
+}
+
+static ds_status check_mla(const char* fn, const MlaArgs& a) {
+  const std::string f(fn);
+  DS_REQUIRE(a.n_q >= 0 && a.kv_rows >= 0, DS_ERR_INVALID_ARG, f + ": negative size");
+  DS_REQUIRE(a.topk >= 1 && a.topk <= 2048, DS_ERR_INVALID_ARG, f + ": topk must be in [1, 2048]");
+  DS_REQUIRE(a.n_heads >= 1 && a.d_latent >= 1 && a.d_rope >= 0, DS_ERR_INVALID_ARG,
+             f + ": bad head/latent dims");
+  if (a.n_q > 0)
+    DS_REQUIRE(a.q && a.topk_idx && a.out && (a.kv_rows == 0 || a.kv), DS_ERR_INVALID_ARG,
+               f + ": NULL q/kv/topk_idx/out");
+  DS_REQUIRE(a.out_dtype == DS_F32 || a.out_dtype == DS_BF16, DS_ERR_UNSUPPORTED,
+             f + ": out must be f32 or bf16");
+  if (a.q_dtype == DS_F32) {
+    DS_REQUIRE(a.kv_dtype == DS_F32 && a.out_dtype == DS_F32, DS_ERR_UNSUPPORTED,
+               f + ": f32 queries need f32 kv and f32 out");
+    DS_REQUIRE(a.n_heads <= 128 && a.d_latent + a.d_rope <= 640, DS_ERR_UNSUPPORTED,
+               f + ": f32 path supports n_heads <= 128, d_latent + d_rope <= 640");
+  } else if (a.q_dtype == DS_BF16) {
+    DS_REQUIRE(a.kv_dtype == DS_BF16 || a.kv_dtype == DS_FP8_E4M3FN, DS_ERR_UNSUPPORTED,
+               f + ": bf16 queries need bf16 or fp8 kv");
+    DS_REQUIRE(a.n_heads % 32 == 0 && a.n_heads <= 128 && a.d_latent == 512 && a.d_rope == 64,
+               DS_ERR_UNSUPPORTED,
+               f + ": bf16 path supports n_heads % 32 == 0 (<= 128), d_latent 512, d_rope 64");
+  } else {
+    return fail(DS_ERR_UNSUPPORTED, f + ": q must be f32 or bf16");
+  }
+  if (a.kv_dtype == DS_FP8_E4M3FN)
+    DS_REQUIRE(a.kv_scale != nullptr, DS_ERR_INVALID_ARG, f + ": fp8 kv needs kv_scale");
+  return DS_OK;
+}
+
+ds_status sparse_mla_prefill(const void* q, ds_dtype q_dtype, const void* kv,
+                             ds_dtype kv_dtype, const float* kv_scale, int64_t kv_rows,
+                             const int32_t* topk_idx, int32_t n_q, int32_t n_heads,
+                             int32_t d_latent, int32_t d_rope, int32_t topk,
+                             float sm_scale, void* out, ds_dtype out_dtype, float* lse,
+                             hipStream_t stream) {
+  MlaArgs a{q, q_dtype, kv, kv_dtype, kv_scale, kv_rows, topk_idx, n_q, n_heads, d_latent,
+            d_rope, topk, sm_scale, out, out_dtype, lse, 1, nullptr};
+  ds_status st = check_mla("sparse_mla_prefill", a);
+  if (st != DS_OK) return st;
+  return launch_sparse_mla(a, stream);
+}
+
+size_t sparse_mla_workspace_size(int32_t n_q, int32_t n_heads, int32_t d_latent,
+                                 int32_t topk) {
+  if (n_q <= 0 || n_heads <= 0 || d_latent <= 0 || topk <= 0) return 256;
+  return mla_partials_bytes(n_q, n_heads, d_latent, mla_decode_splits(n_q, topk));
+}
+
+ds_status sparse_mla_decode(const void* q, ds_dtype q_dtype, const void* kv,
+                            ds_dtype kv_dtype, const float* kv_scale, int64_t kv_rows,
+                            const int32_t* topk_idx, int32_t n_q, int32_t n_heads,
+                            int32_t d_latent, int32_t d_rope, int32_t topk, float sm_scale,
+                            void* out, ds_dtype out_dtype, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  MlaArgs a{q, q_dtype, kv, kv_dtype, kv_scale, kv_rows, topk_idx, n_q, n_heads, d_latent,
+            d_rope, topk, sm_scale, out, out_dtype, lse, 1, ws};
+  ds_status st = check_mla("sparse_mla_decode", a);
+  if (st != DS_OK) return st;
+  DS_REQUIRE(ws != nullptr && ws_bytes >= sparse_mla_workspace_size(n_q, n_heads, d_latent, topk),
+             DS_ERR_WORKSPACE, "sparse_mla_decode: workspace smaller than sparse_mla_workspace_size()");
+  if (q_dtype != DS_F32) a.n_splits = mla_decode_splits(n_q, topk);
+  return launch_sparse_mla(a, stream);
+}
+
+}  // extern "C"

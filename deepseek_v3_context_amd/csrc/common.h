@@ -1,0 +1,156 @@
+// Internal helpers shared by the ds32cp HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "ds32cp.h"
+
+namespace ds32cp {
+
+// ----------------------------------------------------------------- errors
+// Per-thread last error text (read through ds_last_error()).
+void set_error(const std::string& msg);
+ds_status fail(ds_status code, const std::string& msg);
+// Checks the launch that just happened on the calling thread.
+ds_status check_launch(const char* what);
+
+// ----------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kFp8BlockRows = 128;
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return static_cast<uint16_t>(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
+}
+
+// Two OCP e4m3fn codes (bytes 0,1 of `word`, or bytes 2,3 when kHi) ->
+// two floats.  gfx950's conversion instructions use the OCP formats.
+template <bool kHi>
+__device__ __forceinline__ float2 fp8x2_to_f32(uint32_t word) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v2f r = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), kHi);
+  return make_float2(r.x, r.y);
+}
+
+// Four e4m3fn codes -> four bfloat16 bit patterns, exactly (every e4m3fn
+// value is representable in bfloat16, so truncating the float is exact).
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t word) {
+  float2 lo = fp8x2_to_f32<false>(word);
+  float2 hi = fp8x2_to_f32<true>(word);
+  uint2 out;
+  out.x = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
+  out.y = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+  return out;
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key);
+// -0.0 is folded onto +0.0 so that equal scores compare equal.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ------------------------------------------------------------ XCD mapping
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Remap a linear workgroup id so that XCD x receives a contiguous run
+// of logical ids: ids that share operands then share that XCD's L2.
+// `grid` must be a multiple of 8.
+__device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t bid, uint32_t grid) {
+  const uint32_t per_xcd = grid >> 3;
+  return (bid & 7u) * per_xcd + (bid >> 3);
+}
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// --------------------------------------------------------- launch helpers
+// (declared here, defined in the kernel sources; all return ds_status)
+ds_status launch_split_metadata(const int32_t* cu, int32_t B, int32_t T, int32_t cp,
+                                int32_t r, int32_t n, int32_t* local_cu,
+                                int32_t* batch_idx, int32_t* global_idx,
+                                int32_t* kv_start, int32_t* kv_len,
+                                hipStream_t s);
+ds_status launch_row_gather_rr(const void* src, void* dst, int32_t n, int32_t cp,
+                               int32_t r, int64_t row_bytes, hipStream_t s);
+ds_status launch_rerange(const void* src, void* dst, int32_t T, int32_t cp,
+                         int32_t slot_rows, int64_t row_bytes, hipStream_t s);
+
+struct IndexerArgs {
+  const void* q_idx;
+  ds_dtype q_dtype;
+  const float* w;
+  const void* k_idx;
+  ds_dtype k_dtype;
+  const float* k_scale;
+  int64_t k_rows;
+  const int32_t* kv_start;
+  const int32_t* kv_len;
+  const int32_t* q_req;
+  const int32_t* page_table;
+  int32_t n_req, page_size, max_pages;
+  int32_t n_q, h_idx, d_idx, max_kv_len;
+  float* scores;
+  int64_t score_stride;
+};
+ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  const float* scores;
+  int64_t score_stride;
+  const int32_t* kv_start;
+  const int32_t* kv_len;
+  const int32_t* q_req;
+  const int32_t* page_table;
+  int32_t n_req, page_size, max_pages;
+  int64_t k_rows;
+  int32_t n_q, max_kv_len, topk;
+  int32_t* topk_idx;
+  float* topk_score;
+};
+ds_status launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct MlaArgs {
+  const void* q;
+  ds_dtype q_dtype;
+  const void* kv;
+  ds_dtype kv_dtype;
+  const float* kv_scale;
+  int64_t kv_rows;
+  const int32_t* topk_idx;
+  int32_t n_q, n_heads, d_latent, d_rope, topk;
+  float sm_scale;
+  void* out;
+  ds_dtype out_dtype;
+  float* lse;
+  int32_t n_splits;   // > 1: split each query's rows (decode variant)
+  void* ws;           // partials for n_splits > 1
+};
+ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s);
+size_t mla_partials_bytes(int32_t n_q, int32_t n_heads, int32_t d_latent,
+                          int32_t n_splits);
+int32_t mla_decode_splits(int32_t n_q, int32_t topk);
+
+}  // namespace ds32cp

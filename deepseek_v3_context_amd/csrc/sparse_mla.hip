@@ -1,0 +1,482 @@
+// Step 5: sparse latent attention (MLA) over each query's selected rows.
+//
+// Sources: "[RFC]: Parallel strategy for Deepseek v3.2 like models" --
+// comment thread (each query attends only to its top-k KV entries instead
+// of all KV), "Pros" (all heads stay on one rank, so the attention is a
+// dense, high-intensity contraction); "Model Parallel Strategy Analysis",
+// common-errors table (MLA's compressed KV is one latent vector per
+// token, shared by every head).  Reading (the pages give no formula):
+// absorbed latent form, key = the full latent row (d_latent + d_rope),
+// value = its first d_latent columns,
+//   out[j,h,:] = sum_s softmax_s(sm_scale * <q[j,h,:], kv[s,:]>) kv[s,:d_latent]
+//   lse[j,h]   = log sum_s exp(sm_scale * <q[j,h,:], kv[s,:]>).
+//
+// bf16/fp8 path (d_latent 512, d_rope 64, heads a multiple of 32): one
+// workgroup per (query, split of its selected rows) with one wave per 32
+// heads (two groups of 16 that share every K and V fragment read).  The selected rows are gathered 64 at a time into LDS (one copy
+// serves all heads, as key for QK and as value for PV), and every wave runs
+// a flash-style loop with MFMA v_mfma_f32_16x16x32_bf16:
+//   S^T[key, head] = K[key, :] . Q[head, :]     A = K (LDS), B = Q (regs)
+//   O^T[c, head]  += V^T[c, key] . P^T[key, head]
+// The transposed form makes the QK output layout (one head per lane, four
+// keys per lane) exactly the B operand layout PV needs, so P never leaves
+// registers; O^T (2 x 16 heads x 512) stays in 256 accumulator registers
+// per lane and each lane owns one head per group, so the online-softmax
+// rescale is one scalar per lane and group.  fp8 rows are widened to bf16 exactly in LDS and their
+// per-block scale multiplies the logits of that key and its softmax weight
+// before PV (both in fp32).
+//
+// Decode (few queries) splits each query's selected rows over several
+// workgroups that write unnormalised partial outputs with their running
+// max and sum; a combine kernel merges them by log-sum-exp.
+#include <stdlib.h>
+
+#include "common.h"
+
+namespace ds32cp {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------------ fp32
+// One workgroup per (query, head): logits of every selected row in LDS,
+// then a block softmax and one output column per thread.
+__global__ void __launch_bounds__(256)
+mla_f32_kernel(MlaArgs a) {
+  extern __shared__ float smem[];
+  const int D = a.d_latent + a.d_rope;
+  float* qh = smem;               // [D]
+  float* logit = smem + D;        // [topk]
+  int32_t* rows = reinterpret_cast<int32_t*>(logit + a.topk);   // [topk]
+  __shared__ float red[256 / kWave];
+  __shared__ float sh_max, sh_sum;
+
+  const int32_t j = blockIdx.x;
+  const int32_t h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* q = static_cast<const float*>(a.q) +
+                   (static_cast<int64_t>(j) * a.n_heads + h) * D;
+  const float* kv = static_cast<const float*>(a.kv);
+  for (int i = tid; i < D; i += blockDim.x) qh[i] = q[i];
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int s = tid; s < a.topk; s += blockDim.x) {
+    int32_t r = a.topk_idx[static_cast<int64_t>(j) * a.topk + s];
+    if (r >= a.kv_rows) r = -1;
+    rows[s] = r;
+    float l = -INFINITY;
+    if (r >= 0) {
+      const float* k = kv + static_cast<int64_t>(r) * D;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = fmaf(qh[d], k[d], dot);
+      l = dot * a.sm_scale;
+    }
+    logit[s] = l;
+    mx = fmaxf(mx, l);
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    float m = red[0];
+    for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w) m = fmaxf(m, red[w]);
+    sh_max = m;
+  }
+  __syncthreads();
+  const float m = sh_max;
+  float sum = 0.f;
+  for (int s = tid; s < a.topk; s += blockDim.x) {
+    const float p = rows[s] >= 0 ? expf(logit[s] - m) : 0.f;
+    logit[s] = p;
+    sum += p;
+  }
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < static_cast<int>(blockDim.x / kWave); ++w) t += red[w];
+    sh_sum = t;
+  }
+  __syncthreads();
+  const float total = sh_sum;
+  const float inv = total > 0.f ? 1.f / total : 0.f;
+  float* out = static_cast<float*>(a.out) + (static_cast<int64_t>(j) * a.n_heads + h) * a.d_latent;
+  for (int c = tid; c < a.d_latent; c += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < a.topk; ++s) {
+      if (rows[s] < 0) continue;
+      acc = fmaf(logit[s], kv[static_cast<int64_t>(rows[s]) * D + c], acc);
+    }
+    out[c] = acc * inv;
+  }
+  if (a.lse && tid == 0)
+    a.lse[static_cast<int64_t>(j) * a.n_heads + h] = total > 0.f ? m + logf(total) : -INFINITY;
+}
+
+// --------------------------------------------------------- MFMA constants
+constexpr int kMlaDl = 512;
+constexpr int kMlaDr = 64;
+constexpr int kMlaD = kMlaDl + kMlaDr;            // 576
+constexpr int kMlaKSteps = kMlaD / 32;            // 18 QK steps of K = 32
+constexpr int kMlaCBlocks = kMlaDl / 16;          // 32 output column blocks
+constexpr int kMlaTile = 64;                      // selected rows per tile
+constexpr int kMlaRowBytes = kMlaD * 2;           // 1152 (bf16 row)
+constexpr int kMlaRowChunks = kMlaRowBytes / 16;  // 72
+constexpr int kMlaLdsRow = kMlaRowBytes + 16;     // padded LDS row stride
+
+// Byte offset of 16-byte chunk `c` of tile row `r`.  The 16-byte pad makes
+// consecutive rows start 36 banks apart, so 16 lanes reading one chunk of
+// 16 consecutive rows (K fragments) and 16 lanes reading 4 rows x 32 bytes
+// (transposed V fragments) both hit distinct banks, and every fragment
+// address is a per-lane base plus a compile-time offset.
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * kMlaLdsRow + (c << 4);
+}
+
+// Lazy rescaling: the running reference max of a head only moves when a
+// tile's max exceeds it by more than 2^kRescaleLog2, so that exp2 of any
+// logit minus the reference stays below 2^8 and the 256-register output
+// accumulator is rescaled only on the rare tiles that raise the max.
+constexpr float kRescaleLog2 = 8.f;
+
+// 16-head groups per wave.
+#ifndef DS32CP_MLA_GROUPS
+#define DS32CP_MLA_GROUPS 1
+#endif
+constexpr int kMlaGroups = DS32CP_MLA_GROUPS;
+
+template <bool kFp8, bool kTrV, int kG>
+__global__ void __launch_bounds__(kWave * 8 / kG)
+mla_mfma_kernel(MlaArgs a, int32_t keys_per_split) {
+  __shared__ __align__(16) uint8_t tile[kMlaTile * kMlaLdsRow];
+  __shared__ int32_t rows[kMlaTile];
+  __shared__ float kscale[kMlaTile];
+  __shared__ int32_t any_valid;
+
+  const int32_t j = blockIdx.x / a.n_splits;
+  const int32_t split = blockIdx.x - j * a.n_splits;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nthreads = blockDim.x;
+  const int grp = lane >> 4;                      // 0..3
+  // this lane's heads: one per 16-head group of the wave
+  const int hbase = wave * 16 * kG + (lane & 15);
+
+  const int32_t s_begin = split * keys_per_split;
+  int32_t s_end = s_begin + keys_per_split;
+  s_end = s_end < a.topk ? s_end : a.topk;
+
+  // Q^T fragments (B operand): head h, dims 32*ks + 8*grp + 0..7.
+  bf16x8 qf[kG][kMlaKSteps];
+#pragma unroll
+  for (int g2 = 0; g2 < kG; ++g2) {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
+                        (static_cast<int64_t>(j) * a.n_heads + hbase + 16 * g2) * kMlaD + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < kMlaKSteps; ++ks)
+      qf[g2][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
+  }
+
+  f32x4 o[kG][kMlaCBlocks];
+  float m_ref[kG];   // reference max (log2 domain)
+  float l_run[kG];   // sum of exp2(logit - m_ref)
+#pragma unroll
+  for (int g2 = 0; g2 < kG; ++g2) {
+    m_ref[g2] = -INFINITY;
+    l_run[g2] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < kMlaCBlocks; ++cb) o[g2][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float scale2 = a.sm_scale * kLog2e;
+
+  for (int32_t t0 = s_begin; t0 < s_end; t0 += kMlaTile) {
+    // ---- gather the tile's rows into LDS
+    if (tid < kMlaTile) {
+      const int32_t s = t0 + tid;
+      int32_t r = s < s_end ? a.topk_idx[static_cast<int64_t>(j) * a.topk + s] : -1;
+      if (r >= a.kv_rows) r = -1;
+      rows[tid] = r;
+      kscale[tid] = (kFp8 && r >= 0) ? a.kv_scale[r / kFp8BlockRows] : 1.f;
+      const uint64_t b = __ballot(r >= 0);
+      if (tid == 0) any_valid = b != 0ull;
+    }
+    __syncthreads();
+    if (!any_valid) {
+      __syncthreads();
+      continue;
+    }
+    if constexpr (kFp8) {
+      constexpr int kPieces = kMlaTile * (kMlaD / 16);   // 16 codes per piece
+      for (int piece = tid; piece < kPieces; piece += nthreads) {
+        const int r = piece / (kMlaD / 16);
+        const int c8 = piece - r * (kMlaD / 16);
+        const int32_t row = rows[r];
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row >= 0)
+          v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv) +
+                                              static_cast<int64_t>(row) * kMlaD + c8 * 16);
+        const uint2 a0 = fp8x4_to_bf16x4(v.x), a1 = fp8x4_to_bf16x4(v.y);
+        const uint2 a2 = fp8x4_to_bf16x4(v.z), a3 = fp8x4_to_bf16x4(v.w);
+        *reinterpret_cast<uint4*>(&tile[tile_off(r, 2 * c8)]) = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        *reinterpret_cast<uint4*>(&tile[tile_off(r, 2 * c8 + 1)]) = make_uint4(a2.x, a2.y, a3.x, a3.y);
+      }
+    } else {
+      constexpr int kPieces = kMlaTile * kMlaRowChunks;
+      for (int piece = tid; piece < kPieces; piece += nthreads) {
+        const int r = piece / kMlaRowChunks;
+        const int c = piece - r * kMlaRowChunks;
+        const int32_t row = rows[r];
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row >= 0)
+          v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv) +
+                                              static_cast<int64_t>(row) * kMlaRowBytes + c * 16);
+        *reinterpret_cast<uint4*>(&tile[tile_off(r, c)]) = v;
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for 4 blocks of 16 keys, both head groups
+    f32x4 st[kG][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int g2 = 0; g2 < kG; ++g2) st[g2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = kb * 16 + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < kMlaKSteps; ++ks) {
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&tile[tile_off(r, ks * 4 + grp)]));
+#pragma unroll
+        for (int g2 = 0; g2 < kG; ++g2)
+          st[g2][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g2][ks], st[g2][kb], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax; this lane: one head per group, keys 16*kb + 4*grp + i
+    bf16x8 pb[kG][2];
+#pragma unroll
+    for (int g2 = 0; g2 < kG; ++g2) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb * 16 + grp * 4 + i;
+          float l = st[g2][kb][i] * scale2;
+          if constexpr (kFp8) l *= kscale[key];
+          l = rows[key] >= 0 ? l : -INFINITY;
+          st[g2][kb][i] = l;
+          mx = fmaxf(mx, l);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // move the reference only when needed (uniform over the wave)
+      const bool need = mx > m_ref[g2] + kRescaleLog2;
+      if (__ballot(need)) {
+        const float m_new = need ? mx : m_ref[g2];
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[g2] - m_new);   // 0 when m_ref = -inf
+        l_run[g2] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < kMlaCBlocks; ++cb) o[g2][cb] *= alpha;
+        m_ref[g2] = m_new;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = __builtin_amdgcn_exp2f(st[g2][kb][i] - m_ref[g2]);
+          psum += p;
+          if constexpr (kFp8) p *= kscale[kb * 16 + grp * 4 + i];   // fold row scale into P
+          pb[g2][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(p);
+        }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l_run[g2] += psum;
+    }
+
+    // ---- O^T += V^T P^T, two steps of 32 keys; one V fragment feeds both
+    //      head groups
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const int r0 = (2 * kp) * 16 + grp * 4;       // keys r0..r0+3
+      const int r1 = (2 * kp + 1) * 16 + grp * 4;   // keys r1..r1+3
+#pragma unroll
+      for (int cb = 0; cb < kMlaCBlocks; ++cb) {
+        bf16x8 vf;
+        if constexpr (kTrV) {
+          // ds_read_b64_tr_b16: in each 16-lane group, lane i names 4
+          // consecutive bf16 of row (base + i/4), columns 4*(i%4)..+3 of
+          // the 16-column block; lane i receives column i of the 4 rows.
+          const int li = lane & 15;
+          const int chunk = 2 * cb + ((li & 3) >> 1);
+          const int sub = (li & 1) * 8;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(&tile[tile_off(r0 + (li >> 2), chunk) + sub]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(&tile[tile_off(r1 + (li >> 2), chunk) + sub]));
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          vf = __builtin_bit_cast(bf16x8, both);
+        } else {
+          const int c = cb * 16 + (lane & 15);        // value column
+          const int chunk = c >> 3;
+          const int within = (c & 7) * 2;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vf[i] = *reinterpret_cast<const __bf16*>(&tile[tile_off(r0 + i, chunk) + within]);
+            vf[4 + i] = *reinterpret_cast<const __bf16*>(&tile[tile_off(r1 + i, chunk) + within]);
+          }
+        }
+#pragma unroll
+        for (int g2 = 0; g2 < kG; ++g2)
+          o[g2][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[g2][kp], o[g2][cb], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int g2 = 0; g2 < kG; ++g2) {
+    const int h = hbase + 16 * g2;
+    if (a.n_splits == 1) {
+      const float inv = l_run[g2] > 0.f ? 1.f / l_run[g2] : 0.f;
+      const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + grp * 4;
+      if (a.out_dtype == DS_BF16) {
+        uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
+#pragma unroll
+        for (int cb = 0; cb < kMlaCBlocks; ++cb) {
+          uint2 pk;
+          pk.x = f32_to_bf16_bits(o[g2][cb][0] * inv) |
+                 (static_cast<uint32_t>(f32_to_bf16_bits(o[g2][cb][1] * inv)) << 16);
+          pk.y = f32_to_bf16_bits(o[g2][cb][2] * inv) |
+                 (static_cast<uint32_t>(f32_to_bf16_bits(o[g2][cb][3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(out + cb * 16) = pk;
+        }
+      } else {
+        float* out = static_cast<float*>(a.out) + obase;
+#pragma unroll
+        for (int cb = 0; cb < kMlaCBlocks; ++cb)
+          *reinterpret_cast<float4*>(out + cb * 16) =
+              make_float4(o[g2][cb][0] * inv, o[g2][cb][1] * inv, o[g2][cb][2] * inv,
+                          o[g2][cb][3] * inv);
+      }
+      if (a.lse && grp == 0)
+        a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
+            l_run[g2] > 0.f ? (m_ref[g2] + log2f(l_run[g2])) * kLn2 : -INFINITY;
+    } else {
+      // partials: O (unnormalised, fp32) [n_q, n_splits, H, Dl]; (m, l) [.., 2]
+      float* po = static_cast<float*>(a.ws) +
+                  ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * kMlaDl +
+                  grp * 4;
+#pragma unroll
+      for (int cb = 0; cb < kMlaCBlocks; ++cb)
+        *reinterpret_cast<float4*>(po + cb * 16) =
+            make_float4(o[g2][cb][0], o[g2][cb][1], o[g2][cb][2], o[g2][cb][3]);
+      if (grp == 0) {
+        float* pml = static_cast<float*>(a.ws) +
+                     static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl +
+                     ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * 2;
+        pml[0] = m_ref[g2];
+        pml[1] = l_run[g2];
+      }
+    }
+  }
+}
+
+// Merge split partials: one workgroup per (query, head), one thread per
+// output column pair.
+__global__ void __launch_bounds__(256)
+mla_combine_kernel(MlaArgs a) {
+  const int32_t j = blockIdx.x;
+  const int32_t h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* pml = static_cast<const float*>(a.ws) +
+                     static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl;
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s)
+    M = fmaxf(M, pml[((static_cast<int64_t>(j) * a.n_splits + s) * a.n_heads + h) * 2]);
+  float Lsum = 0.f;
+  float acc0 = 0.f, acc1 = 0.f;
+  const int c = tid * 2;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const int64_t ph = (static_cast<int64_t>(j) * a.n_splits + s) * a.n_heads + h;
+    const float ms = pml[ph * 2];
+    const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    Lsum += pml[ph * 2 + 1] * wgt;
+    const float2 v = *reinterpret_cast<const float2*>(static_cast<const float*>(a.ws) + ph * kMlaDl + c);
+    acc0 = fmaf(v.x, wgt, acc0);
+    acc1 = fmaf(v.y, wgt, acc1);
+  }
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + c;
+  if (a.out_dtype == DS_BF16) {
+    uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
+    *reinterpret_cast<uint32_t*>(out) =
+        f32_to_bf16_bits(acc0 * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc1 * inv)) << 16);
+  } else {
+    float* out = static_cast<float*>(a.out) + obase;
+    *reinterpret_cast<float2*>(out) = make_float2(acc0 * inv, acc1 * inv);
+  }
+  if (a.lse && tid == 0)
+    a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
+        Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+}
+
+// ------------------------------------------------------------------ host
+// Value fragments are read with the LDS transpose instruction unless
+// DS32CP_MLA_SCALAR_V=1 selects the element-wise reads (same results; used
+// to cross-check the transpose layout).
+static bool mla_transpose_reads() {
+  const char* e = getenv("DS32CP_MLA_SCALAR_V");
+  return !(e && e[0] == '1');
+}
+
+int32_t mla_decode_splits(int32_t n_q, int32_t topk) {
+  // enough workgroups to cover the 256 CUs; at least 4 tiles per split
+  const int32_t tiles = static_cast<int32_t>(ceil_div(topk, kMlaTile));
+  int32_t want = static_cast<int32_t>(ceil_div(256, n_q > 0 ? n_q : 1));
+  int32_t max_splits = tiles / 4 > 0 ? tiles / 4 : 1;
+  want = want < max_splits ? want : max_splits;
+  return want > 0 ? want : 1;
+}
+
+size_t mla_partials_bytes(int32_t n_q, int32_t n_heads, int32_t d_latent,
+                          int32_t n_splits) {
+  return sizeof(float) * static_cast<size_t>(n_q) * n_splits * n_heads *
+         (static_cast<size_t>(d_latent) + 2);
+}
+
+ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
+  if (a.n_q == 0) return DS_OK;
+  if (a.q_dtype == DS_F32) {
+    const int D = a.d_latent + a.d_rope;
+    const size_t smem = sizeof(float) * (D + a.topk) + sizeof(int32_t) * a.topk;
+    dim3 grid(a.n_q, a.n_heads);
+    mla_f32_kernel<<<grid, 256, smem, s>>>(a);
+    return check_launch("sparse_mla (f32)");
+  }
+  const int threads = kWave * (a.n_heads / (16 * kMlaGroups));
+  const int32_t per_split =
+      static_cast<int32_t>(round_up(ceil_div(a.topk, a.n_splits), kMlaTile));
+  const int64_t blocks = static_cast<int64_t>(a.n_q) * a.n_splits;
+  const bool tr = mla_transpose_reads();
+  if (a.kv_dtype == DS_FP8_E4M3FN) {
+    if (tr) mla_mfma_kernel<true, true, kMlaGroups><<<blocks, threads, 0, s>>>(a, per_split);
+    else mla_mfma_kernel<true, false, kMlaGroups><<<blocks, threads, 0, s>>>(a, per_split);
+  } else {
+    if (tr) mla_mfma_kernel<false, true, kMlaGroups><<<blocks, threads, 0, s>>>(a, per_split);
+    else mla_mfma_kernel<false, false, kMlaGroups><<<blocks, threads, 0, s>>>(a, per_split);
+  }
+  ds_status st = check_launch("sparse_mla");
+  if (st != DS_OK || a.n_splits == 1) return st;
+  dim3 cgrid(a.n_q, a.n_heads);
+  mla_combine_kernel<<<cgrid, kMlaDl / 2, 0, s>>>(a);
+  return check_launch("sparse_mla combine");
+}
+
+}  // namespace ds32cp

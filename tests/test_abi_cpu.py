@@ -1,0 +1,110 @@
+"""C-ABI library checks that need no GPU.
+
+The library must load, export every entry point include/ds32cp.h declares,
+and reject bad arguments on the host before any launch (so these calls
+never reach the device).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import round_robin_cp as rr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds32cp.h")
+
+ds = pytest.importorskip("deepseek_v3_context_amd",
+                         reason="libds32cp.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_five_path_calls():
+    names = _declared()
+    for n in ("cp_split_metadata", "kv_rerange", "indexer_topk", "sparse_mla_prefill",
+              "sparse_mla_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ds.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version_and_local_count():
+    assert ds.abi_version() == 1
+    for T in (0, 1, 7, 8, 9, 8000, 25305, 65536):
+        for cp in (1, 3, 8):
+            for r in range(cp):
+                assert ds.cp_local_count(T, cp, r) == rr.local_count(T, cp, r)
+    with pytest.raises(ValueError):
+        ds.cp_local_count(10, 4, 4)
+
+
+lib = ds._lib.lib
+
+
+def _err():
+    return lib.ds_last_error().decode()
+
+
+def test_split_rejects_bad_arguments_before_launch():
+    assert lib.cp_split_metadata(None, 1, 8, 0, 0, *([None] * 7), 0, None) == 1
+    assert lib.cp_split_metadata(None, 1, 8, 4, 4, *([None] * 7), 0, None) == 1
+    assert "cp_rank" in _err()
+    assert lib.cp_split_metadata(None, 0, 8, 4, 0, *([None] * 7), 0, None) == 1
+    # row gather without destination
+    assert lib.cp_split_metadata(ctypes.c_void_p(16), 1, 8, 4, 0, None, None, None, None,
+                                 None, ctypes.c_void_p(16), None, 4, None) == 1
+
+
+def test_rerange_rejects_bad_arguments_before_launch():
+    assert lib.kv_rerange(None, 2, 8, 4, 16, None, None) == 1          # NULL buffers
+    assert lib.kv_rerange(ctypes.c_void_p(256), 1, 8, 4, 16, ctypes.c_void_p(4096), None) == 1
+    assert "slot_rows" in _err()
+    assert lib.kv_rerange(ctypes.c_void_p(256), 2, 8, 4, 0, ctypes.c_void_p(4096), None) == 1
+    # overlapping src/dst
+    assert lib.kv_rerange(ctypes.c_void_p(256), 2, 8, 4, 16, ctypes.c_void_p(300), None) == 1
+    assert "overlap" in _err()
+
+
+def _p(x=256):
+    return ctypes.c_void_p(x)
+
+
+def test_indexer_rejects_unsupported_and_small_workspace():
+    args = lambda q_dt, k_dt, h, d, topk, ws: (  # noqa: E731
+        _p(), q_dt, _p(), _p(), k_dt, None, 100, _p(), _p(), None, None, 0, 0, 0,
+        4, h, d, 100, topk, _p(), None, _p(), ws, None)
+    big = ds.indexer_topk_workspace_size(4, 100)
+    assert lib.indexer_topk(*args(1, 1, 32, 128, 16, big)) == 2       # bf16 needs 64x128
+    assert lib.indexer_topk(*args(1, 0, 64, 128, 16, big)) == 2       # bf16 q + f32 k
+    assert lib.indexer_topk(*args(1, 2, 64, 128, 16, big)) == 1       # fp8 without scale
+    assert lib.indexer_topk(*args(1, 1, 64, 128, 0, big)) == 1        # topk out of range
+    assert lib.indexer_topk(*args(1, 1, 64, 128, 4096, big)) == 1
+    assert lib.indexer_topk(*args(1, 1, 64, 128, 16, big - 1)) == 3   # workspace
+    assert "workspace" in _err()
+
+
+def test_mla_rejects_unsupported_dims_and_workspace():
+    base = lambda q_dt, kv_dt, H, dl, dr, out_dt: (  # noqa: E731
+        _p(), q_dt, _p(), kv_dt, None, 100, _p(), 4, H, dl, dr, 64, 0.1, _p(), out_dt, None)
+    assert lib.sparse_mla_prefill(*base(1, 1, 48, 512, 64, 1), None) == 2   # heads % 32
+    assert lib.sparse_mla_prefill(*base(1, 1, 128, 256, 64, 1), None) == 2  # latent dims
+    assert lib.sparse_mla_prefill(*base(0, 1, 16, 64, 16, 0), None) == 2    # f32 q, bf16 kv
+    assert lib.sparse_mla_prefill(*base(1, 2, 128, 512, 64, 1), None) == 1  # fp8 w/o scale
+    need = ds.sparse_mla_workspace_size(4, 128, 512, 64)
+    assert lib.sparse_mla_decode(*base(1, 1, 128, 512, 64, 1), _p(), need - 1, None) == 3
+
+
+def test_workspace_sizes():
+    assert ds.indexer_topk_workspace_size(1000, 8000) >= 1000 * 8000 * 4
+    assert ds.sparse_mla_workspace_size(32, 128, 512, 2048) >= 32 * 128 * 512 * 4

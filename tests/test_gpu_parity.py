@@ -1,0 +1,268 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Gates (written out here, derived in the design doc):
+
+* split metadata, row gather, rank-concatenated buffer and rerange:
+  bit-exact;
+* indexer scores: |gpu - oracle64| <= 5e-5 (fp32 accumulation of bf16
+  products; scores are O(0.1)) and positions past kv_len never written;
+* top-k: same count, no duplicates, every index causal, and every element of
+  the symmetric difference has an oracle score within 1e-3 of the oracle's
+  k-th score; rows with at most k causal keys select exactly all of them;
+* sparse MLA, on the GPU's own top-k set: max-abs <= 2e-2 (bf16 KV) or
+  6e-2 (fp8 KV), and relative max-abs <= 1e-2 (bf16) / 3e-2 (fp8); fp32
+  inputs: max-abs <= 1e-4; lse within 1e-3.
+
+Small workloads are checked on every query row; the full-size ones (the
+launch configuration bench.py times) on sampled rows: the first and last
+four plus 24 seeded random rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pipeline as opl
+from oracle import round_robin_cp as orr
+from synth import draw_decode, draw_prefill, get
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import deepseek_v3_context_amd as ds  # noqa: E402
+    from tests import gpu_path as gp  # noqa: E402
+
+SCORE_ATOL = 5e-5
+TOPK_BAND = 1e-3
+
+
+def _sample_rows(n, seed):
+    if n <= 64:
+        return list(range(n))
+    rng = np.random.default_rng(seed)
+    pick = set(range(4)) | set(range(n - 4, n)) | set(rng.choice(n, 24, replace=False).tolist())
+    return sorted(pick)
+
+
+def _mla_gate(wl):
+    if wl.kv_fmt == "f32":
+        return 1e-4, 1e-4
+    if wl.kv_fmt == "fp8":
+        return 6e-2, 3e-2
+    return 2e-2, 1e-2
+
+
+def _check_rows(wl, g, orc_sel, rows, inp, kv_data, kv_scale):
+    kth_misses = 0
+    gidx_rows = []
+    for i, (j, s) in enumerate(zip(rows, orc_sel)):
+        L = s["key_rows"].size
+        # ---- S3 scores
+        sc = g["scores"][j]
+        assert np.all(np.abs(sc[:L] - s["scores64"]) <= SCORE_ATOL), \
+            f"row {j}: score err {np.abs(sc[:L] - s['scores64']).max():.3e}"
+        assert np.all(np.isnan(sc[L:])), f"row {j}: wrote past kv_len"
+        # ---- S4 top-k
+        gi = g["topk_idx"][j]
+        valid = gi[gi >= 0]
+        assert (gi[valid.size:] == -1).all(), f"row {j}: -1 padding not at the end"
+        assert valid.size == min(wl.topk, L), f"row {j}: count {valid.size} vs {min(wl.topk, L)}"
+        assert np.unique(valid).size == valid.size, f"row {j}: duplicate indices"
+        pos_of = {int(x): p for p, x in enumerate(s["key_rows"].tolist())}
+        assert all(int(x) in pos_of for x in valid), f"row {j}: non-causal index"
+        o = s["topk_idx"][s["topk_idx"] >= 0]
+        diff = set(valid.tolist()) ^ set(o.tolist())
+        if L <= wl.topk:
+            assert not diff, f"row {j}: must select every causal key"
+        else:
+            kth = s["scores64"][s["sel_pos"][-1]]
+            far = [x for x in diff if abs(s["scores64"][pos_of[x]] - kth) > TOPK_BAND]
+            assert not far, f"row {j}: {len(far)} selections outside the tie band"
+            kth_misses += len(diff) // 2
+        gs = g["topk_score"][j][: valid.size]
+        exp = s["scores64"][[pos_of[int(x)] for x in valid]]
+        assert np.all(np.abs(gs - exp) <= SCORE_ATOL), f"row {j}: selected score mismatch"
+        gidx_rows.append(gi)
+    # ---- S5 sparse MLA on the GPU's own selection
+    ref_o, ref_l = opl.sparse_mla_rows(rows, gidx_rows, inp["q"], wl.act_fmt, kv_data,
+                                       wl.kv_fmt, kv_scale, wl.scale, wl.d_latent)
+    abs_gate, rel_gate = _mla_gate(wl)
+    for key_o, key_l in (("out", "lse"), ("out_prefill_kernel", "lse_prefill_kernel")):
+        if key_o not in g:
+            continue
+        got_o = g[key_o][rows]
+        err = np.abs(got_o - ref_o).max()
+        rel = err / np.abs(ref_o).max()
+        lerr = np.abs(g[key_l][rows] - ref_l).max()
+        gp.say(f"  {wl.name} {key_o}: max|dO|={err:.3e} rel={rel:.3e} max|dlse|={lerr:.3e}"
+               f" top-k swaps within band={kth_misses}")
+        assert err <= abs_gate and rel <= rel_gate, (err, rel)
+        assert lerr <= 1e-3, lerr
+
+
+PREFILL_SMALL = ["tiny_prefill_t256_cp4", "tiny_prefill_dense", "tiny_prefill_bf16",
+                 "small_prefill_3req_cp4", "small_prefill_3req_cp4_fp8",
+                 "small_prefill_topk2048", "small_prefill_sharp"]
+PREFILL_FULL = ["prefill_t8000_cp8", "prefill_6req_t25305_cp8", "prefill_t65536_cp8_fp8"]
+
+
+def _check_prefill(name, all_rows):
+    wl = get(name)
+    T, cp, r = wl.num_tokens, wl.cp_size, wl.cp_rank
+    n = orr.local_count(T, cp, r)
+    inp = draw_prefill(wl, n)
+    g = gp.run_prefill(wl, inp)
+    om = orr.split_metadata(inp["cu_seqlens"], cp, r)
+    # S1: metadata and the row gather, bit-exact
+    for key in ("global_idx", "batch_idx", "local_cu", "kv_start", "kv_len"):
+        assert np.array_equal(g[key], om[key]), key
+    assert np.array_equal(g["rows"], orr.split_rows(inp["input_ids"], cp, r))
+    # all-gather stand-in built by the split kernel == the oracle's rank concat
+    kv_bytes = np.ascontiguousarray(inp["kv"]).view(np.uint8).reshape(T, -1)
+    cat = orr.rank_concat(kv_bytes, cp, g["slot"], pad_value=0xFF)
+    assert np.array_equal(g["kv_cat_bytes"].reshape(cat.shape), cat)
+    # S2: rerange restores logical order, bit-exact
+    assert np.array_equal(g["kv_bytes"].reshape(T, -1), orr.rerange(cat, T, cp, g["slot"]))
+    assert np.array_equal(g["kv_bytes"].reshape(T, -1), kv_bytes)
+    ki_bytes = np.ascontiguousarray(inp["k_idx"]).view(np.uint8).reshape(T, -1)
+    assert np.array_equal(g["ki_bytes"].reshape(T, -1), ki_bytes)
+    rows = list(range(n)) if all_rows else _sample_rows(n, wl.seed)
+    gp.say(f"  oracle on {len(rows)} of {n} rows")
+    sel = opl.indexer_topk_rows(rows, om, inp["q_idx"], wl.act_fmt, inp["w"], inp["k_idx"],
+                                wl.kv_fmt, inp["k_idx_scale"], wl.topk)
+    _check_rows(wl, g, sel, rows, inp, inp["kv"], inp["kv_scale"])
+
+
+@pytest.mark.parametrize("name", PREFILL_SMALL)
+def test_prefill_small_all_rows(name):
+    _check_prefill(name, all_rows=True)
+
+
+@pytest.mark.parametrize("name", PREFILL_FULL)
+def test_prefill_full_size_sampled_rows(name):
+    _check_prefill(name, all_rows=False)
+
+
+def _check_decode(name, all_rows):
+    wl = get(name)
+    inp = draw_decode(wl)
+    g = gp.run_decode(wl, inp)
+    meta = opl.decode_metadata(inp["lengths"])
+    rows = list(range(wl.n_req)) if all_rows else _sample_rows(wl.n_req, wl.seed)
+    sel = opl.indexer_topk_rows(rows, meta, inp["q_idx"], wl.act_fmt, inp["w"], inp["k_idx"],
+                                wl.kv_fmt, inp["k_idx_scale"], wl.topk,
+                                page_table=inp["page_table"], page_size=wl.page_size)
+    _check_rows(wl, g, sel, rows, inp, inp["kv"], inp["kv_scale"])
+
+
+def test_decode_small_all_rows():
+    _check_decode("small_decode_paged", all_rows=True)
+
+
+def test_decode_full_size_all_requests():
+    _check_decode("decode_32req_paged", all_rows=True)
+
+
+# ------------------------------------------------------------------ edges
+
+def test_ranks_without_tokens_and_empty_requests():
+    cu = torch.tensor([0, 3, 3, 5], dtype=torch.int32, device=gp.DEV)
+    for r in range(8):
+        meta = ds.cp_split_metadata(cu, 5, 8, r)
+        om = orr.split_metadata([0, 3, 3, 5], 8, r)
+        torch.cuda.synchronize()
+        for key in ("global_idx", "batch_idx", "local_cu", "kv_start", "kv_len"):
+            assert np.array_equal(meta[key].cpu().numpy(), om[key]), (r, key)
+
+
+@pytest.mark.parametrize("row_shape,dtype", [((3,), torch.uint8), ((1,), torch.int32),
+                                             ((2,), torch.int32), ((80,), torch.float32),
+                                             ((576,), torch.uint8), ((128,), torch.bfloat16)])
+def test_rerange_host_built_concat_all_row_sizes(row_shape, dtype):
+    elem = torch.empty((), dtype=dtype).element_size()
+    rb = int(np.prod(row_shape)) * elem
+    for T, cp in ((1, 4), (13, 4), (1001, 8), (4096, 3)):
+        x = np.random.default_rng(T + 1).integers(0, 256, size=(T, rb), dtype=np.uint8)
+        slot = orr.local_count(T, cp, 0)
+        cat = orr.rank_concat(x, cp, slot, pad_value=0xFF)
+        src = torch.from_numpy(cat).to(gp.DEV).view(dtype).reshape((cp * slot,) + row_shape)
+        got = ds.kv_rerange(src, slot, T, cp)
+        torch.cuda.synchronize()
+        assert np.array_equal(gp.raw_bytes(got).reshape(T, rb), orr.rerange(cat, T, cp, slot))
+
+
+def test_mla_empty_and_out_of_range_rows():
+    wl = get("tiny_prefill_bf16")
+    rng = np.random.default_rng(5)
+    q = torch.randn(3, 128, 576, device=gp.DEV).bfloat16() / 24
+    kv = torch.randn(50, 576, device=gp.DEV).bfloat16() / 24
+    idx = torch.full((3, 64), -1, dtype=torch.int32, device=gp.DEV)
+    idx[1, :5] = torch.tensor([3, 7, 50, 1000, 9], dtype=torch.int32)   # 50, 1000 out of range
+    idx[2, 10:20] = torch.from_numpy(rng.permutation(50)[:10].astype(np.int32)).to(gp.DEV)
+    out, lse = ds.sparse_mla_prefill(q, kv, idx, wl.scale, 512)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(torch.isinf(lse[0])) and torch.all(lse[0] < 0)
+    qn = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    kvn = kv.view(torch.int16).cpu().numpy().view(np.uint16)
+    for j, sel in ((1, [3, 7, 9]), (2, idx[2, 10:20].cpu().tolist())):
+        ro, rl = opl.sparse_mla_rows([j], [np.array(sel)], qn, "bf16", kvn, "bf16", None,
+                                     wl.scale, 512)
+        err = np.abs(out[j].float().cpu().numpy() - ro[0]).max()
+        assert err <= 1e-2 * np.abs(ro[0]).max(), err
+        assert np.abs(lse[j].cpu().numpy() - rl[0]).max() <= 1e-3
+
+
+def test_mla_transposed_value_reads_match_elementwise_reads(monkeypatch):
+    wl = get("small_prefill_3req_cp4")
+    n = 40
+    q = torch.randn(n, 128, 576, device=gp.DEV).bfloat16() / 24
+    kv = torch.randn(700, 576, device=gp.DEV).bfloat16() / 24
+    idx = torch.stack([torch.randperm(700, device=gp.DEV)[:256] for _ in range(n)]).int()
+    idx[5, 100:] = -1
+    a, la = ds.sparse_mla_prefill(q, kv, idx, wl.scale, 512)
+    monkeypatch.setenv("DS32CP_MLA_SCALAR_V", "1")
+    b, lb = ds.sparse_mla_prefill(q, kv, idx, wl.scale, 512)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_decode_page_boundaries():
+    # lengths 1, 63, 64, 65, 129 exercise partial and exact pages
+    lengths = np.array([1, 63, 64, 65, 129], dtype=np.int32)
+    ps = 64
+    pages = [-(-int(L) // ps) for L in lengths]
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(sum(pages)).astype(np.int32)
+    table = np.full((5, max(pages)), -1, dtype=np.int32)
+    off = 0
+    for i, k in enumerate(pages):
+        table[i, :k] = perm[off: off + k]
+        off += k
+    rows = sum(pages) * ps
+    ki = (rng.standard_normal((rows, 128)) / np.sqrt(128)).astype(np.float32)
+    qi = (rng.standard_normal((5, 64, 128)) / np.sqrt(128)).astype(np.float32)
+    w = (rng.standard_normal((5, 64)) / 8).astype(np.float32)
+    from synth.draw import to_bf16_bits
+    ki_b, qi_b = to_bf16_bits(ki), to_bf16_bits(qi)
+    meta = ds.decode_metadata(torch.from_numpy(lengths).to(gp.DEV))
+    idx, _ = ds.indexer_topk(gp.to_dev(qi_b, "bf16"), torch.from_numpy(w).to(gp.DEV),
+                             gp.to_dev(ki_b, "bf16"), meta["kv_start"], meta["kv_len"],
+                             int(lengths.max()), 16, q_req=meta["q_req"],
+                             page_table=torch.from_numpy(table).to(gp.DEV), page_size=ps)
+    torch.cuda.synchronize()
+    om = opl.decode_metadata(lengths)
+    sel = opl.indexer_topk_rows(range(5), om, qi_b, "bf16", w, ki_b, "bf16", None, 16,
+                                page_table=table, page_size=ps)
+    gi = idx.cpu().numpy()
+    for j, s in enumerate(sel):
+        assert set(gi[j][gi[j] >= 0].tolist()) == set(s["topk_idx"][s["topk_idx"] >= 0].tolist())
+
+
+def test_integer_outputs_repeatable():
+    wl = get("small_prefill_3req_cp4")
+    n = orr.local_count(wl.num_tokens, wl.cp_size, wl.cp_rank)
+    inp = draw_prefill(wl, n)
+    a = gp.run_prefill(wl, inp, want_scores=False)
+    b = gp.run_prefill(wl, inp, want_scores=False)
+    assert np.array_equal(np.sort(a["topk_idx"], 1), np.sort(b["topk_idx"], 1))
+    assert np.array_equal(a["out"], b["out"])
