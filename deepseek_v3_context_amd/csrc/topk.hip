@@ -11,10 +11,10 @@
 // 32-bit keys and the k-th largest key is found by four 8-bit radix passes
 // (LDS histogram + one-wave suffix scan per pass).  Rows that fit are
 // cached in LDS so the passes never return to HBM; longer rows stream from
-// L2/HBM.  The final pass writes every key above the threshold (slot by
-// LDS atomic, order free) and the lowest-position keys equal to it (slot
-// by an ordered ballot scan), so the selected set is exactly the
-// tie-to-lower-position set.
+// L2/HBM.  A final ordered pass (ballot + per-wave counts) writes the
+// selected positions in ascending order: every key above the threshold and
+// the lowest-position keys equal to it, so the selected set is exactly the
+// tie-to-lower-position set and the output is deterministic.
 #include "common.h"
 
 namespace ds32cp {
@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(kTkThreads)
 topk_kernel(TopkArgs a, int32_t cache_keys) {
   extern __shared__ uint32_t cache[];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_digit, sh_remaining, gt_slot;
+  __shared__ uint32_t sh_digit, sh_remaining;
   __shared__ uint32_t wave_eq[kTkWaves];
 
   const int32_t j = blockIdx.x;
@@ -110,39 +110,51 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   }
 
   // prefix is now the k-th largest key; `remaining` copies of it are taken.
-  const uint32_t n_gt = static_cast<uint32_t>(a.topk) - remaining;
-  if (tid == 0) gt_slot = 0;
-  __syncthreads();
-  uint32_t eq_seen = 0;
+  // One ordered pass writes every selected position in ascending order:
+  // keys above the threshold, and the first `remaining` keys equal to it.
+  uint32_t taken = 0, eq_seen = 0;
   for (int32_t base = 0; base < L; base += kTkThreads) {
     const int32_t t = base + tid;
     const uint32_t u = t < L ? key_at(t) : 0u;
     const bool gt = t < L && u > prefix;
     const bool eq = t < L && u == prefix;
-    const uint64_t ball = __ballot(eq);
-    if (lane == 0) wave_eq[wave] = static_cast<uint32_t>(__popcll(ball));
+    const uint64_t ball_eq = __ballot(eq);
+    // an equal key is taken when fewer than `remaining` equal keys precede it
+    const uint32_t eq_rank_in_wave = static_cast<uint32_t>(__popcll(ball_eq & ((1ull << lane) - 1ull)));
+    if (lane == 0) wave_eq[wave] = static_cast<uint32_t>(__popcll(ball_eq));
     __syncthreads();
-    uint32_t before = eq_seen, total = 0;
+    uint32_t eq_before = eq_seen;
+    uint32_t eq_total = 0;
 #pragma unroll
     for (int w = 0; w < kTkWaves; ++w) {
       const uint32_t cnt = wave_eq[w];
-      before += w < wave ? cnt : 0u;
-      total += cnt;
+      eq_before += w < wave ? cnt : 0u;
+      eq_total += cnt;
     }
-    eq_seen += total;
-    int32_t slot = -1;
-    if (gt) {
-      slot = static_cast<int32_t>(atomicAdd(&gt_slot, 1u));
-    } else if (eq) {
-      const uint32_t rank = before + static_cast<uint32_t>(
-          __popcll(ball & ((1ull << lane) - 1ull)));
-      if (rank < remaining) slot = static_cast<int32_t>(n_gt + rank);
-    }
-    if (slot >= 0 && slot < a.topk) {
-      out_idx[slot] = static_cast<int32_t>(topk_key_row(a, req, kv0 + t));
-      if (out_score) out_score[slot] = order_key_to_float(u);
-    }
+    const bool take = gt || (eq && eq_before + eq_rank_in_wave < remaining);
+    const uint64_t ball_take = __ballot(take);
+    __syncthreads();   // wave_eq is reused below
+    if (lane == 0) wave_eq[wave] = static_cast<uint32_t>(__popcll(ball_take));
     __syncthreads();
+    uint32_t take_before = taken, take_total = 0;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+      const uint32_t cnt = wave_eq[w];
+      take_before += w < wave ? cnt : 0u;
+      take_total += cnt;
+    }
+    if (take) {
+      const uint32_t slot = take_before +
+          static_cast<uint32_t>(__popcll(ball_take & ((1ull << lane) - 1ull)));
+      if (slot < static_cast<uint32_t>(a.topk)) {
+        out_idx[slot] = static_cast<int32_t>(topk_key_row(a, req, kv0 + t));
+        if (out_score) out_score[slot] = order_key_to_float(u);
+      }
+    }
+    taken += take_total;
+    eq_seen += eq_total;
+    __syncthreads();
+    if (taken >= static_cast<uint32_t>(a.topk)) break;   // uniform: all threads agree
   }
 }
 
