@@ -13,10 +13,10 @@
 // with heads as the M dimension and keys as N, so that one lane's output
 // column is one key and the head reduction (after ReLU and the per-head
 // weight) is 32 in-register FMAs plus one cross-half swap.
-//   * prefill: a workgroup owns 8 consecutive queries (2 per wave, their
-//     A fragments held in registers for the whole chunk) and a chunk of
-//     absolute key rows; 32-key tiles are staged once in LDS and shared by
-//     the 4 waves (double-buffered through registers).  Queries of one
+//   * prefill: a workgroup of 8 waves owns 8 consecutive queries (one per
+//     wave, A fragments and head weights in registers for the whole chunk)
+//     and a chunk of absolute key rows; 64-key tiles are gathered into LDS
+//     by DMA, double-buffered, and shared by the 8 waves.  Queries of one
 //     workgroup may belong to different requests: each masks its own
 //     causal range on write.
 //   * decode: keys are paged per request, so a workgroup owns one query
@@ -25,6 +25,8 @@
 // fp8 keys are widened to bf16 exactly; the per-block scale is positive
 // and multiplies the whole score of its key (ReLU commutes with a
 // positive factor), so it is applied once per key after the head sum.
+#include <type_traits>
+
 #include "common.h"
 
 namespace ds32cp {
@@ -92,11 +94,7 @@ constexpr int kIxHeads = 64;
 constexpr int kIxDim = 128;
 constexpr int kIxKSteps = kIxDim / 16;        // K = 16 per MFMA
 constexpr int kIxRowBlocks = kIxHeads / 32;   // M = 32 per MFMA
-constexpr int kIxWaves = 4;
-constexpr int kIxQPerWave = 2;
-constexpr int kIxQBlock = kIxWaves * kIxQPerWave;   // 8 queries / workgroup
-constexpr int kIxTileKeys = 32;
-constexpr int kIxRowBytes = kIxDim * 2 + 16;       // padded LDS row (bank spread)
+constexpr int kIxWaves = 4;                  // decode kernel: waves per workgroup
 
 // A fragment of v_mfma_f32_32x32x16_bf16 for heads [32*rb, 32*rb+32) and
 // dims [16*ks, 16*ks+16): lane l holds head 32*rb + l%32, dims
@@ -108,9 +106,10 @@ __device__ __forceinline__ bf16x8 load_q_frag(const uint16_t* q_row0, int rb, in
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Weighted ReLU head-sum of one 64-head x 32-key accumulator pair.  Output
-// element i of lane l sits at head 8*(i/4) + 4*(l/32) + i%4 (+32*rb), key
-// l%32; after the cross-half swap every lane holds its key's full sum.
+// Weighted ReLU head-sum of one 64-head x 32-key accumulator pair (decode
+// kernel).  Output element i of lane l sits at head 8*(i/4) + 4*(l/32) +
+// i%4 (+32*rb), key l%32; after the cross-half swap every lane holds its
+// key's full sum.
 __device__ __forceinline__ float head_sum(const f32x16 (&acc)[kIxRowBlocks],
                                           const float* w_heads, int lane) {
   float v = 0.f;
@@ -126,25 +125,84 @@ __device__ __forceinline__ float head_sum(const f32x16 (&acc)[kIxRowBlocks],
   return v;
 }
 
-// ---------------------------------------------------- prefill, MFMA path
+// --------------------------------------------- prefill, pipelined path
+// A workgroup of 8 waves owns 8 consecutive queries (one per wave: A
+// fragments in 64 VGPRs, the 64 head weights of the query in 32 VGPRs) and
+// a chunk of absolute key rows.  64-key tiles are gathered straight into
+// LDS with global_load_lds_dwordx4 (no VGPRs), double-buffered so that the
+// gather of tile t+1 overlaps the MFMAs of tile t; every wave reads the
+// shared tile's B fragments from LDS.  Two waves per SIMD.
+constexpr int kIxPWaves = 8;
+constexpr int kIxPTile = 64;                       // keys per tile
 template <bool kFp8>
-__global__ void __launch_bounds__(256)
-indexer_prefill_mfma_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks,
-                            int32_t chunk_keys, uint32_t grid) {
-  __shared__ __align__(16) uint8_t ktile[2][kIxTileKeys * kIxRowBytes];
-  __shared__ float wl[kIxQBlock][kIxHeads];
-  __shared__ int64_t q_lo[kIxQBlock], q_hi[kIxQBlock];
+struct IxTile {
+  static constexpr int kRowBytes = kFp8 ? kIxDim : 2 * kIxDim;   // 128 / 256
+  static constexpr int kLdsRow = kRowBytes + 16;                  // padded
+  static constexpr int kChunksPerRow = kLdsRow / 16;              // 9 / 17
+  static constexpr int kChunks = kIxPTile * kChunksPerRow;        // 576 / 1088
+  static constexpr int kInst = (kChunks + kWave - 1) / kWave;     // 9 / 17
+  static constexpr int kBytes = kInst * kWave * 16;               // LDS bytes per buffer
+};
 
+__shared__ __align__(16) uint8_t g_ix_buf0[IxTile<false>::kBytes];
+__shared__ __align__(16) uint8_t g_ix_buf1[IxTile<false>::kBytes];
+
+template <int B>
+__device__ __forceinline__ uint8_t* ix_buf() {
+  return B ? g_ix_buf1 : g_ix_buf0;
+}
+
+// Gathers key rows [base, base + 64) into buffer B (rows past k_rows read
+// row 0; their scores are never stored).
+template <int B, bool kFp8>
+__device__ __forceinline__ void ix_issue_tile(const uint8_t* keys, int64_t k_rows, int64_t base,
+                                              int wave, int lane) {
+  using TL = IxTile<kFp8>;
+  for (int m = wave; m < TL::kInst; m += kIxPWaves) {
+    const int P = m * kWave + lane;
+    const int r = P / TL::kChunksPerRow;
+    const int c = P - r * TL::kChunksPerRow;
+    int64_t row = base + r;
+    row = (row < k_rows && r < kIxPTile) ? row : 0;
+    const int cc = c < TL::kRowBytes / 16 ? c : TL::kRowBytes / 16 - 1;
+    __builtin_amdgcn_global_load_lds(
+        keys + row * TL::kRowBytes + cc * 16,
+        (__attribute__((address_space(3))) void*)(ix_buf<B>() + m * kWave * 16), 16, 0, 0);
+  }
+}
+
+// B fragment of v_mfma_f32_32x32x16_bf16 for key column (lane & 31) of the
+// tile block `nb` and dims 16*ks + 8*(lane/32) + 0..7.
+template <bool kFp8>
+__device__ __forceinline__ bf16x8 ix_bfrag(const uint8_t* tile, int nb, int ks, int lane) {
+  using TL = IxTile<kFp8>;
+  const uint8_t* row = tile + (nb * 32 + (lane & 31)) * TL::kLdsRow;
+  if constexpr (kFp8) {
+    const uint2 c = *reinterpret_cast<const uint2*>(row + ks * 16 + (lane >> 5) * 8);
+    const uint2 lo = fp8x4_to_bf16x4(c.x);
+    const uint2 hi = fp8x4_to_bf16x4(c.y);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  } else {
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const uint4*>(row + ks * 32 + (lane >> 5) * 16));
+  }
+}
+
+template <bool kFp8>
+__global__ void __launch_bounds__(kWave * kIxPWaves)
+indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks,
+                                 int32_t chunk_keys, uint32_t grid) {
+  __shared__ int64_t q_lo[kIxPWaves], q_hi[kIxPWaves];
   const uint32_t id = xcd_contiguous_id(blockIdx.x, grid);
   if (id >= static_cast<uint32_t>(n_qblocks) * n_chunks) return;
   const int32_t qb = id / n_chunks;
   const int32_t chunk = id - qb * n_chunks;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  if (tid < kIxQBlock) {
-    const int32_t j = qb * kIxQBlock + tid;
+  if (tid < kIxPWaves) {
+    const int32_t j = qb * kIxPWaves + tid;
     int64_t lo = 0, hi = 0;
     if (j < a.n_q) {
       lo = a.kv_start[j];
@@ -156,16 +214,10 @@ indexer_prefill_mfma_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks,
     q_lo[tid] = lo;
     q_hi[tid] = hi;
   }
-  for (int i = tid; i < kIxQBlock * kIxHeads; i += blockDim.x) {
-    const int32_t j = qb * kIxQBlock + i / kIxHeads;
-    wl[i / kIxHeads][i % kIxHeads] =
-        j < a.n_q ? a.w[static_cast<int64_t>(j) * kIxHeads + i % kIxHeads] : 0.f;
-  }
   __syncthreads();
-
   int64_t rlo = INT64_MAX, rhi = 0;
 #pragma unroll
-  for (int i = 0; i < kIxQBlock; ++i) {
+  for (int i = 0; i < kIxPWaves; ++i) {
     if (q_hi[i] > q_lo[i]) {
       rlo = q_lo[i] < rlo ? q_lo[i] : rlo;
       rhi = q_hi[i] > rhi ? q_hi[i] : rhi;
@@ -176,112 +228,76 @@ indexer_prefill_mfma_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks,
   rlo = rlo > c_lo ? rlo : c_lo;
   rhi = rhi < c_hi ? rhi : c_hi;
   if (rlo >= rhi) return;
-  const int64_t t_first = (rlo / kIxTileKeys) * kIxTileKeys;
-  const int32_t n_tiles = static_cast<int32_t>(ceil_div(rhi - t_first, kIxTileKeys));
+  const int64_t t_first = (rlo / kIxPTile) * kIxPTile;
+  const int32_t n_tiles = static_cast<int32_t>(ceil_div(rhi - t_first, kIxPTile));
+  const uint8_t* keys = static_cast<const uint8_t*>(a.k_idx);
+  ix_issue_tile<0, kFp8>(keys, a.k_rows, t_first, wave, lane);
 
-  // A fragments of this wave's two queries, resident for the whole chunk.
-  bf16x8 qa[kIxQPerWave][kIxRowBlocks][kIxKSteps];
-  int64_t my_lo[kIxQPerWave], my_hi[kIxQPerWave];
-  int32_t my_j[kIxQPerWave];
-#pragma unroll
-  for (int s = 0; s < kIxQPerWave; ++s) {
-    const int qi = wave * kIxQPerWave + s;
-    my_j[s] = qb * kIxQBlock + qi;
-    my_lo[s] = q_lo[qi];
-    my_hi[s] = q_hi[qi];
-    const bool live = my_hi[s] > my_lo[s];
+  // this wave's query: A fragments, head weights of the rows this lane's
+  // accumulator elements hold, causal range
+  const int32_t j = qb * kIxPWaves + wave;
+  const int64_t my_lo = q_lo[wave], my_hi = q_hi[wave];
+  const bool live = my_hi > my_lo;
+  bf16x8 qa[kIxRowBlocks][kIxKSteps];
+  float wv[kIxRowBlocks][16];
+  {
     const uint16_t* q0 = static_cast<const uint16_t*>(a.q_idx) +
-                         static_cast<int64_t>(live ? my_j[s] : 0) * kIxHeads * kIxDim;
+                         static_cast<int64_t>(live ? j : 0) * kIxHeads * kIxDim;
+    const float* w0 = a.w + static_cast<int64_t>(live ? j : 0) * kIxHeads;
 #pragma unroll
-    for (int rb = 0; rb < kIxRowBlocks; ++rb)
+    for (int rb = 0; rb < kIxRowBlocks; ++rb) {
 #pragma unroll
-      for (int ks = 0; ks < kIxKSteps; ++ks)
-        qa[s][rb][ks] = live ? load_q_frag(q0, rb, ks, lane)
-                             : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      for (int ks = 0; ks < kIxKSteps; ++ks) qa[rb][ks] = load_q_frag(q0, rb, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wv[rb][i] = w0[rb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
+    }
   }
+  float* srow = a.scores + static_cast<int64_t>(live ? j : 0) * a.score_stride;
 
-  // Cooperative tile load: bf16 keys 32 x 256 B (two 16-byte pieces per
-  // thread); fp8 keys 32 x 128 B (one 16-byte piece, widened to 32 bytes).
-  constexpr int kPieces = kFp8 ? 1 : 2;
-  uint4 stage[kPieces];
-  auto fetch = [&](int64_t base) {
+  auto step = [&](auto bufc, int t) {
+    constexpr int B = decltype(bufc)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gather of tile t landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();         // every wave's; tile t-1 fully consumed
+    asm volatile("" ::: "memory");
+    const int64_t base = t_first + static_cast<int64_t>(t) * kIxPTile;
+    if (t + 1 < n_tiles) ix_issue_tile<1 - B, kFp8>(keys, a.k_rows, base + kIxPTile, wave, lane);
+    if (!live || base >= my_hi || base + kIxPTile <= my_lo) return;
+    const uint8_t* tile = ix_buf<B>();
 #pragma unroll
-    for (int u = 0; u < kPieces; ++u) {
-      const int piece = tid + u * 256;
-      const int key = kFp8 ? (piece >> 3) : (piece >> 4);
-      const int part = kFp8 ? (piece & 7) : (piece & 15);
-      const int64_t row = base + key;
-      if (row < a.k_rows) {
-        const uint8_t* src = static_cast<const uint8_t*>(a.k_idx) +
-                             row * (kFp8 ? kIxDim : 2 * kIxDim) + part * 16;
-        stage[u] = *reinterpret_cast<const uint4*>(src);
-      } else {
-        stage[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < kPieces; ++u) {
-      const int piece = tid + u * 256;
-      if constexpr (kFp8) {
-        const int key = piece >> 3, part = piece & 7;
-        uint8_t* dst = &ktile[buf][key * kIxRowBytes + part * 32];
-        const uint2 a0 = fp8x4_to_bf16x4(stage[u].x);
-        const uint2 a1 = fp8x4_to_bf16x4(stage[u].y);
-        const uint2 a2 = fp8x4_to_bf16x4(stage[u].z);
-        const uint2 a3 = fp8x4_to_bf16x4(stage[u].w);
-        *reinterpret_cast<uint4*>(dst) = make_uint4(a0.x, a0.y, a1.x, a1.y);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(a2.x, a2.y, a3.x, a3.y);
-      } else {
-        const int key = piece >> 4, part = piece & 15;
-        *reinterpret_cast<uint4*>(&ktile[buf][key * kIxRowBytes + part * 16]) = stage[u];
-      }
-    }
-  };
-
-  fetch(t_first);
-  for (int32_t t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const int64_t base = t_first + static_cast<int64_t>(t) * kIxTileKeys;
-    commit(buf);
-    __syncthreads();
-    if (t + 1 < n_tiles) fetch(base + kIxTileKeys);
-
-    f32x16 acc[kIxQPerWave][kIxRowBlocks];
-    bool act[kIxQPerWave];
-#pragma unroll
-    for (int s = 0; s < kIxQPerWave; ++s) {
-      act[s] = my_lo[s] < base + kIxTileKeys && base < my_hi[s];
+    for (int nb = 0; nb < 2; ++nb) {
+      if (base + nb * 32 >= my_hi || base + nb * 32 + 32 <= my_lo) continue;
+      f32x16 acc[kIxRowBlocks];
 #pragma unroll
       for (int rb = 0; rb < kIxRowBlocks; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[s][rb][i] = 0.f;
-    }
-    if (act[0] || act[1]) {
-      const uint8_t* krow = &ktile[buf][(lane & 31) * kIxRowBytes + (lane >> 5) * 16];
+        for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+      bf16x8 bcur = ix_bfrag<kFp8>(tile, nb, 0, lane);
 #pragma unroll
       for (int ks = 0; ks < kIxKSteps; ++ks) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 32));
+        bf16x8 bnext = bcur;
+        if (ks + 1 < kIxKSteps) bnext = ix_bfrag<kFp8>(tile, nb, ks + 1, lane);
 #pragma unroll
-        for (int s = 0; s < kIxQPerWave; ++s) {
-          if (!act[s]) continue;
-#pragma unroll
-          for (int rb = 0; rb < kIxRowBlocks; ++rb)
-            acc[s][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s][rb][ks], b, acc[s][rb], 0, 0, 0);
-        }
+        for (int rb = 0; rb < kIxRowBlocks; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], bcur, acc[rb], 0, 0, 0);
+        bcur = bnext;
       }
+      float v = 0.f;
 #pragma unroll
-      for (int s = 0; s < kIxQPerWave; ++s) {
-        if (!act[s]) continue;
-        float v = head_sum(acc[s], wl[wave * kIxQPerWave + s], lane);
-        const int64_t row = base + (lane & 31);
-        if (lane < 32 && row >= my_lo[s] && row < my_hi[s]) {
-          if constexpr (kFp8) v *= a.k_scale[row / kFp8BlockRows];
-          a.scores[static_cast<int64_t>(my_j[s]) * a.score_stride + (row - my_lo[s])] = v;
-        }
+      for (int rb = 0; rb < kIxRowBlocks; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], fmaxf(acc[rb][i], 0.f), v);
+      v += __shfl_xor(v, 32);
+      const int64_t row = base + nb * 32 + (lane & 31);
+      if (lane < 32 && row >= my_lo && row < my_hi) {
+        if constexpr (kFp8) v *= a.k_scale[row / kFp8BlockRows];
+        srow[row - my_lo] = v;
       }
     }
+  };
+  for (int32_t t = 0; t < n_tiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1);
   }
 }
 
@@ -361,7 +377,7 @@ indexer_paged_mfma_kernel(IndexerArgs a, int32_t n_chunks) {
 }
 
 // ------------------------------------------------------------------ host
-static constexpr int32_t kIxChunkKeys = 1024;
+static constexpr int32_t kIxPChunkKeys = 2048;
 
 ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
   if (a.n_q == 0 || a.max_kv_len == 0) return DS_OK;
@@ -379,13 +395,15 @@ ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
     else indexer_paged_mfma_kernel<false><<<blocks, 256, 0, s>>>(a, n_chunks);
     return check_launch("indexer_scores (paged)");
   }
-  const int32_t n_qblocks = static_cast<int32_t>(ceil_div(a.n_q, kIxQBlock));
-  const int32_t n_chunks = static_cast<int32_t>(ceil_div(a.k_rows, kIxChunkKeys));
+  const int32_t n_qblocks = static_cast<int32_t>(ceil_div(a.n_q, kIxPWaves));
+  const int32_t n_chunks = static_cast<int32_t>(ceil_div(a.k_rows, kIxPChunkKeys));
   const uint32_t grid = static_cast<uint32_t>(round_up(static_cast<int64_t>(n_qblocks) * n_chunks, 8));
   if (fp8)
-    indexer_prefill_mfma_kernel<true><<<grid, 256, 0, s>>>(a, n_qblocks, n_chunks, kIxChunkKeys, grid);
+    indexer_prefill_pipelined_kernel<true><<<grid, kWave * kIxPWaves, 0, s>>>(
+        a, n_qblocks, n_chunks, kIxPChunkKeys, grid);
   else
-    indexer_prefill_mfma_kernel<false><<<grid, 256, 0, s>>>(a, n_qblocks, n_chunks, kIxChunkKeys, grid);
+    indexer_prefill_pipelined_kernel<false><<<grid, kWave * kIxPWaves, 0, s>>>(
+        a, n_qblocks, n_chunks, kIxPChunkKeys, grid);
   return check_launch("indexer_scores (prefill)");
 }
 

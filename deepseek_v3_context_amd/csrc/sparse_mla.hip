@@ -31,6 +31,8 @@
 // max and sum; a combine kernel merges them by log-sum-exp.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace ds32cp {
@@ -389,278 +391,316 @@ mla_mfma_kernel(MlaArgs a, int32_t keys_per_split) {
 }
 
 // ------------------------------------------------- bf16 KV, pipelined
-// One workgroup of 8 waves per (query, split); wave w owns heads
-// [16w, 16w+16) (two waves per SIMD: O^T in 128 accumulator registers,
-// S^T in 16, Q^T in 72 VGPRs -- a 32-head wave would need 288 accumulator
-// registers, more than the 256 a wave can hold).  The selected row indices of the split are
-// staged in LDS once; 64-row tiles are gathered straight into LDS with
-// global_load_lds_dwordx4 (no VGPRs), double-buffered: the gather of tile
-// t+1 is in flight while tile t is computed.
-constexpr int kDmaRowChunks = kMlaLdsRow / 16;               // 73 (72 + pad)
-constexpr int kDmaInstPerTile = kMlaTile * kDmaRowChunks / kWave;   // 73
+// One workgroup of kW = n_heads/16 waves per (query, split of its rows).
+//   * QK + softmax: wave w owns heads [16w, 16w+16).  S^T = K Q^T on
+//     v_mfma_f32_16x16x32_bf16 with K from LDS and Q^T (72 VGPRs) in
+//     registers; the online softmax of a head lives in the lane group that
+//     owns it.  The bf16 softmax weights P of every head go to LDS.
+//   * PV: wave w owns output columns [w*512/kW, (w+1)*512/kW) for ALL heads:
+//     O^T[c, h] += V^T[c, key] P^T[key, h], so each V fragment (LDS
+//     transpose read) feeds kW MFMAs and each P fragment 512/kW/16.  O^T
+//     is 128 fp32 accumulator registers per lane whatever kW is.
+// 32-row tiles are gathered straight into LDS (global_load_lds_dwordx4,
+// no VGPRs), double-buffered so the gather of tile t+1 overlaps tile t.
+// Lazy rescaling: a head's reference max moves only when a tile raises it
+// by more than 2^kRescaleLog2; the owner publishes the factor and every
+// wave rescales its columns of that head.
+constexpr int kPipeTile = 32;                                     // rows per tile
+// Padded LDS row of the pipelined kernel: 1184 bytes (74 chunks).  With
+// this stride both the K-fragment reads (16 rows, one chunk) and the V
+// transpose reads (4 rows x 32 bytes per 16-lane group) are free of bank
+// conflicts (measured: 1152 is 4x and 1168 1.5x slower for one of them),
+// and a 32-row tile is exactly 37 DMA wave-instructions.
+constexpr int kPipeRow = kMlaRowBytes + 32;
+constexpr int kDmaRowChunks = kPipeRow / 16;                      // 74 (72 + pad)
+constexpr int kPipeTileChunks = kPipeTile * kDmaRowChunks;        // 2368
+constexpr int kPipeTileInst = kPipeTileChunks / kWave;            // 37
 constexpr int kMlaMaxKeys = 2048;
-#ifndef DS32CP_MLA_PIPE_GROUPS
-#define DS32CP_MLA_PIPE_GROUPS 1
-#endif
-constexpr int kMlaPipeGroups = DS32CP_MLA_PIPE_GROUPS;
 
-__shared__ __align__(16) uint8_t g_mla_buf0[kMlaTile * kMlaLdsRow];
-__shared__ __align__(16) uint8_t g_mla_buf1[kMlaTile * kMlaLdsRow];
+__shared__ __align__(16) uint8_t g_mla_buf0[kPipeTile * kPipeRow];
+__shared__ __align__(16) uint8_t g_mla_buf1[kPipeTile * kPipeRow];
 
 template <int B>
 __device__ __forceinline__ uint8_t* mla_buf() {
   return B ? g_mla_buf1 : g_mla_buf0;
 }
 
-// Gathers tile rows sidx[t0 .. t0+63] into buffer B.  Wave-instruction m
+// Gathers tile rows sidx[t0 .. t0+31] into buffer B.  Wave-instruction m
 // fills LDS chunks [64m, 64m+64) of the padded tile; lane l's chunk is row
-// (64m+l)/73, column (64m+l)%73 (column 72 is padding: it re-reads column
-// 71).  Empty slots (-1) read row 0; their logits are masked and their
-// softmax weight is 0.
-template <int B, int kWaves>
+// (64m+l)/74, column (64m+l)%74 (columns 72, 73 are padding and re-read
+// column 71).  Empty slots (-1) read row 0: their logits are masked and
+// their softmax weight is 0.
+template <int B, int kW>
 __device__ __forceinline__ void mla_issue_tile(const uint8_t* kv, const int32_t* sidx, int t0,
                                                int wave, int lane) {
-  constexpr int kStep = kWaves * kWave;   // chunks between a wave's instructions
-  constexpr int kStepRows = kStep / kDmaRowChunks;
-  constexpr int kStepCols = kStep - kStepRows * kDmaRowChunks;
-  int P = wave * kWave + lane;
-  int r = P / kDmaRowChunks;
-  int c = P - r * kDmaRowChunks;
-  for (int m = wave; m < kDmaInstPerTile; m += kWaves) {
+  for (int m = wave; m < kPipeTileInst; m += kW) {
+    const int P = m * kWave + lane;
+    const int r = P / kDmaRowChunks;
+    const int c = P - r * kDmaRowChunks;
     int32_t row = sidx[t0 + r];
     row = row < 0 ? 0 : row;
     const int cc = c < kMlaRowChunks ? c : kMlaRowChunks - 1;
-    const uint8_t* src = kv + static_cast<int64_t>(row) * kMlaRowBytes + cc * 16;
     __builtin_amdgcn_global_load_lds(
-        src, (__attribute__((address_space(3))) void*)(mla_buf<B>() + m * kWave * 16), 16, 0, 0);
-    c += kStepCols;
-    r += kStepRows;
-    if (c >= kDmaRowChunks) {
-      c -= kDmaRowChunks;
-      r += 1;
-    }
+        kv + static_cast<int64_t>(row) * kMlaRowBytes + cc * 16,
+        (__attribute__((address_space(3))) void*)(mla_buf<B>() + m * kWave * 16), 16, 0, 0);
   }
 }
 
-struct MlaLane {
-  int lane, wave, grp, li;
+template <int kW>
+struct MlaShared {
+  static constexpr int kHeads = 16 * kW;
+  int32_t sidx[kMlaMaxKeys];
+  uint4 p[4][kHeads];          // P^T fragments: [lane group][head] -> 8 bf16
+  float alpha[kHeads];         // per-tile rescale factor of each head
+  int32_t rescale[kW];         // wave w raised a reference max this tile
+  int32_t wave_cnt[kW];        // index compaction scratch
+  float m_fin[kHeads], l_fin[kHeads];
 };
 
-template <bool kTrV, int kG>
-__device__ __forceinline__ void mla_tile_compute(const uint8_t* tile, uint64_t valid,
-                                                 const bf16x8 (&qf)[kG][kMlaKSteps],
-                                                 f32x4 (&o)[kG][kMlaCBlocks], float (&m_ref)[kG],
-                                                 float (&l_run)[kG], float scale2,
-                                                 const MlaLane& L) {
-  // ---- S^T = K Q^T: 4 blocks of 16 keys x 2 head groups
-  f32x4 st[kG][4];
-#pragma unroll
-  for (int g2 = 0; g2 < kG; ++g2)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) st[g2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint8_t* kbase = tile + (L.lane & 15) * kMlaLdsRow + L.grp * 16;
-#pragma unroll
-  for (int ks = 0; ks < kMlaKSteps; ++ks) {
-    bf16x8 kf[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      kf[kb] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(kbase + kb * 16 * kMlaLdsRow + ks * 64));
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int g2 = 0; g2 < kG; ++g2)
-        st[g2][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qf[g2][ks], st[g2][kb], 0, 0, 0);
-  }
-  // ---- online softmax (this lane: one head per group; keys 16kb+4grp+i)
-  bf16x8 pb[kG][2];
-#pragma unroll
-  for (int g2 = 0; g2 < kG; ++g2) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb * 16 + L.grp * 4 + i;
-        const float l = ((valid >> key) & 1ull) ? st[g2][kb][i] * scale2 : -INFINITY;
-        st[g2][kb][i] = l;
-        mx = fmaxf(mx, l);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool need = mx > m_ref[g2] + kRescaleLog2;
-    if (__ballot(need)) {
-      const float m_new = need ? mx : m_ref[g2];
-      const float alpha = __builtin_amdgcn_exp2f(m_ref[g2] - m_new);
-      l_run[g2] *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < kMlaCBlocks; ++cb) o[g2][cb] *= alpha;
-      m_ref[g2] = m_new;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(st[g2][kb][i] - m_ref[g2]);
-        psum += p;
-        pb[g2][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(p);
-      }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run[g2] += psum;
-  }
-  // ---- O^T += V^T P^T (two steps of 32 keys); each V fragment feeds both
-  //      head groups
-#pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {
-    const int r0 = 32 * kp + 4 * L.grp;
-    const uint8_t* vlo = tile + (r0 + (L.li >> 2)) * kMlaLdsRow + ((L.li & 3) >> 1) * 16 + (L.li & 1) * 8;
-    const uint8_t* vhi = vlo + 16 * kMlaLdsRow;
-#pragma unroll
-    for (int cb = 0; cb < kMlaCBlocks; ++cb) {
-      bf16x8 vf;
-      if constexpr (kTrV) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vlo + cb * 32));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vhi + cb * 32));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      } else {
-        const int col = cb * 16 + L.li;
-        const uint8_t* p0 = tile + r0 * kMlaLdsRow + (col >> 3) * 16 + (col & 7) * 2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vf[i] = *reinterpret_cast<const __bf16*>(p0 + i * kMlaLdsRow);
-          vf[4 + i] = *reinterpret_cast<const __bf16*>(p0 + (16 + i) * kMlaLdsRow);
-        }
-      }
-#pragma unroll
-      for (int g2 = 0; g2 < kG; ++g2)
-        o[g2][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[g2][kp], o[g2][cb], 0, 0, 0);
-    }
-  }
-}
-
-// Waits for this tile's gather (own wave, then all waves), starts the next
-// gather into the other buffer, and computes this tile.
-template <int B, bool kTrV, int kG>
-__device__ __forceinline__ void mla_pipeline_step(const uint8_t* kv, const int32_t* sidx,
-                                                  int t, int n_tiles,
-                                                  const bf16x8 (&qf)[kG][kMlaKSteps],
-                                                  f32x4 (&o)[kG][kMlaCBlocks], float (&m_ref)[kG],
-                                                  float (&l_run)[kG], float scale2,
-                                                  const MlaLane& L) {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gather of tile t landed
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();         // ... and every wave's
-  asm volatile("" ::: "memory");
-  if (t + 1 < n_tiles)
-    mla_issue_tile<1 - B, 8 / kG>(kv, sidx, (t + 1) * kMlaTile, L.wave, L.lane);
-  const uint64_t valid = __ballot(sidx[t * kMlaTile + L.lane] >= 0);
-  if (valid == 0ull) return;
-  mla_tile_compute<kTrV, kG>(mla_buf<B>(), valid, qf, o, m_ref, l_run, scale2, L);
-}
-
-template <bool kTrV, int kG>
-__global__ void __launch_bounds__(kWave * 8 / kG)
+template <bool kTrV, int kW>
+__global__ void __launch_bounds__(kWave * kW)
 mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
-  constexpr int kThreads = kWave * 8 / kG;
-  __shared__ int32_t sidx[kMlaMaxKeys];
+  constexpr int kThreads = kWave * kW;
+  constexpr int kHeads = 16 * kW;
+  constexpr int kCols = kMlaDl / kW;          // output columns per wave
+  constexpr int kCB = kCols / 16;             // 16-column blocks per wave
+  __shared__ MlaShared<kW> sh;
+
   const int32_t j = blockIdx.x / a.n_splits;
   const int32_t split = blockIdx.x - j * a.n_splits;
   const int tid = threadIdx.x;
-  MlaLane L;
-  L.lane = tid & 63;
-  L.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  L.grp = L.lane >> 4;
-  L.li = L.lane & 15;
-  const int hbase = L.wave * 16 * kG + L.li;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4;
+  const int li = lane & 15;
+  const int h_own = wave * 16 + li;           // head whose softmax this lane keeps
 
   const int32_t s_begin = split * keys_per_split;
   int32_t s_end = s_begin + keys_per_split;
   s_end = s_end < a.topk ? s_end : a.topk;
   const int32_t n_keys = s_end > s_begin ? s_end - s_begin : 0;
-  const int32_t n_tiles = static_cast<int32_t>(ceil_div(n_keys, kMlaTile));
+  // Stage the split's valid row indices in LDS, compacted to the front in
+  // their given order (ordered ballot scan), so empty slots cost no tiles.
   const int32_t* idx_row = a.topk_idx + static_cast<int64_t>(j) * a.topk + s_begin;
-  for (int i = tid; i < n_tiles * kMlaTile; i += kThreads) {
-    int32_t r = i < n_keys ? idx_row[i] : -1;
-    sidx[i] = (r >= 0 && r < a.kv_rows) ? r : -1;
-  }
-
-  bf16x8 qf[kG][kMlaKSteps];
+  int32_t n_valid = 0;
+  for (int32_t i0 = 0; i0 < n_keys; i0 += kThreads) {
+    const int32_t i = i0 + tid;
+    const int32_t r = i < n_keys ? idx_row[i] : -1;
+    const bool ok = r >= 0 && r < a.kv_rows;
+    const uint64_t ball = __ballot(ok);
+    if (lane == 0) sh.wave_cnt[wave] = static_cast<int32_t>(__popcll(ball));
+    __syncthreads();
+    int32_t before = n_valid, total = 0;
 #pragma unroll
-  for (int g2 = 0; g2 < kG; ++g2) {
+    for (int w = 0; w < kW; ++w) {
+      const int32_t c = sh.wave_cnt[w];
+      before += w < wave ? c : 0;
+      total += c;
+    }
+    if (ok) sh.sidx[before + __popcll(ball & ((1ull << lane) - 1ull))] = r;
+    n_valid += total;
+    __syncthreads();
+  }
+  const int32_t n_tiles = static_cast<int32_t>(ceil_div(n_valid, kPipeTile));
+  for (int32_t i = n_valid + tid; i < n_tiles * kPipeTile; i += kThreads) sh.sidx[i] = -1;
+
+  // Q^T fragments (B operand of QK): head h_own, dims 32*ks + 8*grp + 0..7
+  bf16x8 qf[kMlaKSteps];
+  {
     const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        (static_cast<int64_t>(j) * a.n_heads + hbase + 16 * g2) * kMlaD + L.grp * 8;
+                        (static_cast<int64_t>(j) * a.n_heads + h_own) * kMlaD + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < kMlaKSteps; ++ks)
-      qf[g2][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
   }
-  f32x4 o[kG][kMlaCBlocks];
-  float m_ref[kG], l_run[kG];
+  // O^T[c, h]: column block cb of this wave, head group hg (lane's head
+  // hg*16 + li, columns 16*cb + 4*grp + 0..3 of this wave's range)
+  f32x4 o[kCB][kW];
 #pragma unroll
-  for (int g2 = 0; g2 < kG; ++g2) {
-    m_ref[g2] = -INFINITY;
-    l_run[g2] = 0.f;
+  for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-    for (int cb = 0; cb < kMlaCBlocks; ++cb) o[g2][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int hg = 0; hg < kW; ++hg) o[cb][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f;
   const float scale2 = a.sm_scale * kLog2e;
   const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
-  __syncthreads();   // sidx ready (no gather in flight yet)
-  if (n_tiles > 0) mla_issue_tile<0, 8 / kG>(kv, sidx, 0, L.wave, L.lane);
+  __syncthreads();   // sidx ready; no gather in flight yet
+  if (n_tiles > 0) mla_issue_tile<0, kW>(kv, sh.sidx, 0, wave, lane);
+
+  auto step = [&](auto bufc, int t) {
+    constexpr int B = decltype(bufc)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gather of tile t landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();         // every wave's gather landed; tile t-1 fully consumed
+    asm volatile("" ::: "memory");
+    if (t + 1 < n_tiles) mla_issue_tile<1 - B, kW>(kv, sh.sidx, (t + 1) * kPipeTile, wave, lane);
+    const uint8_t* tile = mla_buf<B>();
+    const int32_t my_row = lane < kPipeTile ? sh.sidx[t * kPipeTile + lane] : -1;
+    const uint64_t valid = __ballot(my_row >= 0);
+
+    // ---- S^T = K Q^T for this wave's 16 heads: 2 blocks of 16 keys; the
+    //      fragments of k-step ks+1 are read while ks is multiplied
+    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const uint8_t* kbase = tile + li * kPipeRow + grp * 16;
+    auto kfrag = [&](int kb, int ks) {
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(kbase + kb * 16 * kPipeRow + ks * 64));
+    };
+    bf16x8 k0 = kfrag(0, 0), k1 = kfrag(1, 0);
+#pragma unroll
+    for (int ks = 0; ks < kMlaKSteps; ++ks) {
+      bf16x8 n0 = k0, n1 = k1;
+      if (ks + 1 < kMlaKSteps) {
+        n0 = kfrag(0, ks + 1);
+        n1 = kfrag(1, ks + 1);
+      }
+      st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], st[0], 0, 0, 0);
+      st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], st[1], 0, 0, 0);
+      k0 = n0;
+      k1 = n1;
+    }
+    // ---- online softmax of head h_own over keys 16*kb + 4*grp + i
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb * 16 + grp * 4 + i;
+        const float l = ((valid >> key) & 1ull) ? st[kb][i] * scale2 : -INFINITY;
+        st[kb][i] = l;
+        mx = fmaxf(mx, l);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = mx > m_ref + kRescaleLog2;
+    float alpha = 1.f;
+    if (need) {
+      alpha = __builtin_amdgcn_exp2f(m_ref - mx);   // 0 on the first raise (m_ref = -inf)
+      m_ref = mx;
+      l_run *= alpha;
+    }
+    const bool wave_rescales = __ballot(need) != 0ull;
+    if (lane < 16) sh.alpha[h_own] = alpha;
+    if (lane == 0) sh.rescale[wave] = wave_rescales;
+    float psum = 0.f;
+    bf16x8 pv;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pw = valid ? __builtin_amdgcn_exp2f(st[kb][i] - m_ref) : 0.f;
+        psum += pw;
+        pv[kb * 4 + i] = static_cast<__bf16>(pw);
+      }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run += psum;
+    sh.p[grp][h_own] = __builtin_bit_cast(uint4, pv);
+    __syncthreads();   // P and the rescale factors of every head are visible
+
+    // ---- rescale this wave's columns of any head whose reference moved
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) any |= sh.rescale[w] != 0;
+    if (any) {
+#pragma unroll
+      for (int hg = 0; hg < kW; ++hg) {
+        const float al = sh.alpha[hg * 16 + li];
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) o[cb][hg] *= al;
+      }
+    }
+    // ---- O^T += V^T P^T for this wave's column blocks, all heads
+    bf16x8 vf[kCB];
+    const uint8_t* vbase = tile + (4 * grp + (li >> 2)) * kPipeRow + ((li & 3) >> 1) * 16 +
+                           (li & 1) * 8 + wave * kCols * 2;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      if constexpr (kTrV) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vbase + cb * 32));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vbase + 16 * kPipeRow + cb * 32));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        vf[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        const int col = wave * kCols + cb * 16 + li;
+        const uint8_t* p0 = tile + 4 * grp * kPipeRow + (col >> 3) * 16 + (col & 7) * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vf[cb][i] = *reinterpret_cast<const __bf16*>(p0 + i * kPipeRow);
+          vf[cb][4 + i] = *reinterpret_cast<const __bf16*>(p0 + (16 + i) * kPipeRow);
+        }
+      }
+    }
+    bf16x8 pf = __builtin_bit_cast(bf16x8, sh.p[grp][li]);
+#pragma unroll
+    for (int hg = 0; hg < kW; ++hg) {
+      bf16x8 pn = pf;
+      if (hg + 1 < kW) pn = __builtin_bit_cast(bf16x8, sh.p[grp][(hg + 1) * 16 + li]);
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+        o[cb][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[cb], pf, o[cb][hg], 0, 0, 0);
+      pf = pn;
+    }
+  };
   for (int32_t t = 0; t < n_tiles; t += 2) {
-    mla_pipeline_step<0, kTrV, kG>(kv, sidx, t, n_tiles, qf, o, m_ref, l_run, scale2, L);
-    if (t + 1 < n_tiles)
-      mla_pipeline_step<1, kTrV, kG>(kv, sidx, t + 1, n_tiles, qf, o, m_ref, l_run, scale2, L);
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  // ---- epilogue (same layout as the staged kernel)
+  // ---- epilogue: owners publish (m, l); every wave writes its columns
+  if (lane < 16) {
+    sh.m_fin[h_own] = m_ref;
+    sh.l_fin[h_own] = l_run;
+  }
+  __syncthreads();
+  const int col0 = wave * kCols + grp * 4;
 #pragma unroll
-  for (int g2 = 0; g2 < kG; ++g2) {
-    const int h = hbase + 16 * g2;
+  for (int hg = 0; hg < kW; ++hg) {
+    const int h = hg * 16 + li;
+    const float lf = sh.l_fin[h];
     if (a.n_splits == 1) {
-      const float inv = l_run[g2] > 0.f ? 1.f / l_run[g2] : 0.f;
-      const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + L.grp * 4;
+      const float inv = lf > 0.f ? 1.f / lf : 0.f;
+      const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + col0;
       if (a.out_dtype == DS_BF16) {
         uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
 #pragma unroll
-        for (int cb = 0; cb < kMlaCBlocks; ++cb) {
+        for (int cb = 0; cb < kCB; ++cb) {
           uint2 pk;
-          pk.x = f32_to_bf16_bits(o[g2][cb][0] * inv) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(o[g2][cb][1] * inv)) << 16);
-          pk.y = f32_to_bf16_bits(o[g2][cb][2] * inv) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(o[g2][cb][3] * inv)) << 16);
+          pk.x = f32_to_bf16_bits(o[cb][hg][0] * inv) |
+                 (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][1] * inv)) << 16);
+          pk.y = f32_to_bf16_bits(o[cb][hg][2] * inv) |
+                 (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][3] * inv)) << 16);
           *reinterpret_cast<uint2*>(out + cb * 16) = pk;
         }
       } else {
         float* out = static_cast<float*>(a.out) + obase;
 #pragma unroll
-        for (int cb = 0; cb < kMlaCBlocks; ++cb)
+        for (int cb = 0; cb < kCB; ++cb)
           *reinterpret_cast<float4*>(out + cb * 16) =
-              make_float4(o[g2][cb][0] * inv, o[g2][cb][1] * inv, o[g2][cb][2] * inv,
-                          o[g2][cb][3] * inv);
+              make_float4(o[cb][hg][0] * inv, o[cb][hg][1] * inv, o[cb][hg][2] * inv,
+                          o[cb][hg][3] * inv);
       }
-      if (a.lse && L.grp == 0)
-        a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
-            l_run[g2] > 0.f ? (m_ref[g2] + log2f(l_run[g2])) * kLn2 : -INFINITY;
     } else {
       float* po = static_cast<float*>(a.ws) +
-                  ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * kMlaDl +
-                  L.grp * 4;
+                  ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * kMlaDl + col0;
 #pragma unroll
-      for (int cb = 0; cb < kMlaCBlocks; ++cb)
+      for (int cb = 0; cb < kCB; ++cb)
         *reinterpret_cast<float4*>(po + cb * 16) =
-            make_float4(o[g2][cb][0], o[g2][cb][1], o[g2][cb][2], o[g2][cb][3]);
-      if (L.grp == 0) {
-        float* pml = static_cast<float*>(a.ws) +
-                     static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl +
-                     ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * 2;
-        pml[0] = m_ref[g2];
-        pml[1] = l_run[g2];
-      }
+            make_float4(o[cb][hg][0], o[cb][hg][1], o[cb][hg][2], o[cb][hg][3]);
+    }
+  }
+  if (lane < 16) {
+    if (a.n_splits == 1) {
+      if (a.lse)
+        a.lse[static_cast<int64_t>(j) * a.n_heads + h_own] =
+            l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : -INFINITY;
+    } else {
+      float* pml = static_cast<float*>(a.ws) +
+                   static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl +
+                   ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h_own) * 2;
+      pml[0] = m_ref;
+      pml[1] = l_run;
     }
   }
 }
@@ -741,10 +781,20 @@ ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
       static_cast<int32_t>(round_up(ceil_div(a.topk, a.n_splits), kMlaTile));
   const int64_t blocks = static_cast<int64_t>(a.n_q) * a.n_splits;
   const bool tr = mla_transpose_reads();
-  if (a.kv_dtype == DS_BF16 && a.n_heads == 128) {
-    constexpr int kG = kMlaPipeGroups;
-    if (tr) mla_bf16_pipelined_kernel<true, kG><<<blocks, kWave * 8 / kG, 0, s>>>(a, per_split);
-    else mla_bf16_pipelined_kernel<false, kG><<<blocks, kWave * 8 / kG, 0, s>>>(a, per_split);
+  if (a.kv_dtype == DS_BF16) {
+    switch (a.n_heads) {
+      case 32:
+        if (tr) mla_bf16_pipelined_kernel<true, 2><<<blocks, kWave * 2, 0, s>>>(a, per_split);
+        else mla_bf16_pipelined_kernel<false, 2><<<blocks, kWave * 2, 0, s>>>(a, per_split);
+        break;
+      case 64:
+        if (tr) mla_bf16_pipelined_kernel<true, 4><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+        else mla_bf16_pipelined_kernel<false, 4><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+        break;
+      default:
+        if (tr) mla_bf16_pipelined_kernel<true, 8><<<blocks, kWave * 8, 0, s>>>(a, per_split);
+        else mla_bf16_pipelined_kernel<false, 8><<<blocks, kWave * 8, 0, s>>>(a, per_split);
+    }
     ds_status st = check_launch("sparse_mla");
     if (st != DS_OK || a.n_splits == 1) return st;
     dim3 cgrid(a.n_q, a.n_heads);
