@@ -188,11 +188,18 @@ __device__ __forceinline__ bf16x8 ix_bfrag(const uint8_t* tile, int nb, int ks, 
   }
 }
 
+constexpr int32_t kIxPChunkKeys = 2048;   // key rows per workgroup
+
 template <bool kFp8>
 __global__ void __launch_bounds__(kWave * kIxPWaves)
 indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks,
-                                 int32_t chunk_keys, uint32_t grid) {
+                                 uint32_t grid) {
+  constexpr int32_t chunk_keys = kIxPChunkKeys;
   __shared__ int64_t q_lo[kIxPWaves], q_hi[kIxPWaves];
+  // scores of the chunk stay in LDS until the end: a global store inside
+  // the tile loop would make every wait for the next tile's gather
+  // (vmcnt counts stores too) also wait for the store to retire
+  __shared__ float sc[kIxPWaves][chunk_keys];
   const uint32_t id = xcd_contiguous_id(blockIdx.x, grid);
   if (id >= static_cast<uint32_t>(n_qblocks) * n_chunks) return;
   const int32_t qb = id / n_chunks;
@@ -264,40 +271,56 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
     if (t + 1 < n_tiles) ix_issue_tile<1 - B, kFp8>(keys, a.k_rows, base + kIxPTile, wave, lane);
     if (!live || base >= my_hi || base + kIxPTile <= my_lo) return;
     const uint8_t* tile = ix_buf<B>();
+    // both 32-key column blocks at once: four independent accumulator
+    // chains per wave keep the MFMA pipe busy
+    f32x16 acc[2][kIxRowBlocks];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if (base + nb * 32 >= my_hi || base + nb * 32 + 32 <= my_lo) continue;
-      f32x16 acc[kIxRowBlocks];
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int rb = 0; rb < kIxRowBlocks; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
-      bf16x8 bcur = ix_bfrag<kFp8>(tile, nb, 0, lane);
+        for (int i = 0; i < 16; ++i) acc[nb][rb][i] = 0.f;
+    bf16x8 b0 = ix_bfrag<kFp8>(tile, 0, 0, lane), b1 = ix_bfrag<kFp8>(tile, 1, 0, lane);
 #pragma unroll
-      for (int ks = 0; ks < kIxKSteps; ++ks) {
-        bf16x8 bnext = bcur;
-        if (ks + 1 < kIxKSteps) bnext = ix_bfrag<kFp8>(tile, nb, ks + 1, lane);
-#pragma unroll
-        for (int rb = 0; rb < kIxRowBlocks; ++rb)
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], bcur, acc[rb], 0, 0, 0);
-        bcur = bnext;
+    for (int ks = 0; ks < kIxKSteps; ++ks) {
+      bf16x8 n0 = b0, n1 = b1;
+      if (ks + 1 < kIxKSteps) {
+        n0 = ix_bfrag<kFp8>(tile, 0, ks + 1, lane);
+        n1 = ix_bfrag<kFp8>(tile, 1, ks + 1, lane);
       }
+#pragma unroll
+      for (int rb = 0; rb < kIxRowBlocks; ++rb) {
+        acc[0][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b0, acc[0][rb], 0, 0, 0);
+        acc[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b1, acc[1][rb], 0, 0, 0);
+      }
+      b0 = n0;
+      b1 = n1;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
       float v = 0.f;
 #pragma unroll
       for (int rb = 0; rb < kIxRowBlocks; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], fmaxf(acc[rb][i], 0.f), v);
+        for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], fmaxf(acc[nb][rb][i], 0.f), v);
       v += __shfl_xor(v, 32);
       const int64_t row = base + nb * 32 + (lane & 31);
-      if (lane < 32 && row >= my_lo && row < my_hi) {
-        if constexpr (kFp8) v *= a.k_scale[row / kFp8BlockRows];
-        srow[row - my_lo] = v;
-      }
+      if (lane < 32 && row >= my_lo && row < my_hi) sc[wave][row - c_lo] = v;
     }
   };
   for (int32_t t = 0; t < n_tiles; t += 2) {
     step(std::integral_constant<int, 0>{}, t);
     if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1);
+  }
+  // write this wave's query's scores of the chunk (contiguous in the row)
+  if (live) {
+    const int64_t lo = my_lo > c_lo ? my_lo : c_lo;
+    const int64_t hi = my_hi < c_hi ? my_hi : c_hi;
+    for (int64_t r = lo + lane; r < hi; r += kWave) {
+      float v = sc[wave][r - c_lo];
+      if constexpr (kFp8) v *= a.k_scale[r / kFp8BlockRows];   // per-row fp8 scale
+      srow[r - my_lo] = v;
+    }
   }
 }
 
@@ -377,7 +400,7 @@ indexer_paged_mfma_kernel(IndexerArgs a, int32_t n_chunks) {
 }
 
 // ------------------------------------------------------------------ host
-static constexpr int32_t kIxPChunkKeys = 2048;
+
 
 ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
   if (a.n_q == 0 || a.max_kv_len == 0) return DS_OK;
@@ -400,10 +423,10 @@ ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
   const uint32_t grid = static_cast<uint32_t>(round_up(static_cast<int64_t>(n_qblocks) * n_chunks, 8));
   if (fp8)
     indexer_prefill_pipelined_kernel<true><<<grid, kWave * kIxPWaves, 0, s>>>(
-        a, n_qblocks, n_chunks, kIxPChunkKeys, grid);
+        a, n_qblocks, n_chunks, grid);
   else
     indexer_prefill_pipelined_kernel<false><<<grid, kWave * kIxPWaves, 0, s>>>(
-        a, n_qblocks, n_chunks, kIxPChunkKeys, grid);
+        a, n_qblocks, n_chunks, grid);
   return check_launch("indexer_scores (prefill)");
 }
 

@@ -425,30 +425,66 @@ __device__ __forceinline__ uint8_t* mla_buf() {
   return B ? g_mla_buf1 : g_mla_buf0;
 }
 
-// Gathers tile rows sidx[t0 .. t0+31] into buffer B.  Wave-instruction m
-// fills LDS chunks [64m, 64m+64) of the padded tile; lane l's chunk is row
-// (64m+l)/74, column (64m+l)%74 (columns 72, 73 are padding and re-read
-// column 71).  Empty slots (-1) read row 0: their logits are masked and
-// their softmax weight is 0.
+// DMA wave-instructions per wave and tile for kW waves (at most 19, for
+// two waves).
+template <int kW>
+struct MlaIssue {
+  static constexpr int kPer = (kPipeTileInst + kW - 1) / kW;
+};
+constexpr int kMlaIssueMax = (kPipeTileInst + 1) / 2;
+
+// One DMA wave-instruction of a tile gather: instruction m of the tile
+// fills LDS chunks [64m, 64m+64); lane l's chunk is row (64m+l)/74, column
+// (64m+l)%74 (columns 72, 73 are padding and re-read column 71).  The lane
+// id is made opaque so this per-lane arithmetic is recomputed at every
+// call instead of being hoisted out of the tile loop: hoisted values get
+// spilled, and a scratch reload between two DMA instructions would wait
+// for the earlier gather (vmcnt counts both).
+__device__ __forceinline__ int mla_gather_row(int m, int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  return (m * kWave + ln) / kDmaRowChunks;
+}
+
+template <int B>
+__device__ __forceinline__ void mla_gather_issue(const uint8_t* kv, int m, int lane,
+                                                 int32_t row) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int P = m * kWave + ln;
+  const int c = P - (P / kDmaRowChunks) * kDmaRowChunks;
+  const int cc = c < kMlaRowChunks ? c : kMlaRowChunks - 1;
+  row = row < 0 ? 0 : row;
+  __builtin_amdgcn_global_load_lds(
+      kv + static_cast<int64_t>(row) * kMlaRowBytes + cc * 16,
+      (__attribute__((address_space(3))) void*)(mla_buf<B>() + m * kWave * 16), 16, 0, 0);
+}
+
+// Gathers a whole tile (rows sidx[t0 .. t0+31]) into buffer B.  Wave-
+// instruction m fills LDS chunks [64m, 64m+64) of the padded tile; lane l's
+// chunk is row (64m+l)/74, column (64m+l)%74 (columns 72, 73 are padding
+// and re-read column 71).  Empty slots (-1) read row 0: their logits are
+// masked and their softmax weight is 0.
 template <int B, int kW>
 __device__ __forceinline__ void mla_issue_tile(const uint8_t* kv, const int32_t* sidx, int t0,
                                                int wave, int lane) {
-  for (int m = wave; m < kPipeTileInst; m += kW) {
-    const int P = m * kWave + lane;
-    const int r = P / kDmaRowChunks;
-    const int c = P - r * kDmaRowChunks;
-    int32_t row = sidx[t0 + r];
-    row = row < 0 ? 0 : row;
-    const int cc = c < kMlaRowChunks ? c : kMlaRowChunks - 1;
-    __builtin_amdgcn_global_load_lds(
-        kv + static_cast<int64_t>(row) * kMlaRowBytes + cc * 16,
-        (__attribute__((address_space(3))) void*)(mla_buf<B>() + m * kWave * 16), 16, 0, 0);
+  int32_t row[kMlaIssueMax];
+#pragma unroll
+  for (int i = 0; i < MlaIssue<kW>::kPer; ++i) {
+    const int m = wave + i * kW;
+    row[i] = m < kPipeTileInst ? sidx[t0 + mla_gather_row(m, lane)] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < MlaIssue<kW>::kPer; ++i) {
+    const int m = wave + i * kW;
+    if (m < kPipeTileInst) mla_gather_issue<B>(kv, m, lane, row[i]);
   }
 }
 
 template <int kW>
 struct MlaShared {
   static constexpr int kHeads = 16 * kW;
+  uint4 qrope[2][4][kHeads];   // rope k-steps of Q^T: [ks-16][lane group][head]
   int32_t sidx[kMlaMaxKeys];
   uint4 p[4][kHeads];          // P^T fragments: [lane group][head] -> 8 bf16
   float alpha[kHeads];         // per-tile rescale factor of each head
@@ -461,7 +497,6 @@ template <bool kTrV, int kW>
 __global__ void __launch_bounds__(kWave * kW)
 mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
   constexpr int kThreads = kWave * kW;
-  constexpr int kHeads = 16 * kW;
   constexpr int kCols = kMlaDl / kW;          // output columns per wave
   constexpr int kCB = kCols / 16;             // 16-column blocks per wave
   __shared__ MlaShared<kW> sh;
@@ -504,14 +539,21 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
   const int32_t n_tiles = static_cast<int32_t>(ceil_div(n_valid, kPipeTile));
   for (int32_t i = n_valid + tid; i < n_tiles * kPipeTile; i += kThreads) sh.sidx[i] = -1;
 
-  // Q^T fragments (B operand of QK): head h_own, dims 32*ks + 8*grp + 0..7
-  bf16x8 qf[kMlaKSteps];
+  // Q^T fragments (B operand of QK): head h_own, dims 32*ks + 8*grp + 0..7;
+  // the 16 latent k-steps stay in VGPRs, the 2 rope k-steps in LDS (this
+  // keeps the wave clear of register spills, whose scratch reloads would
+  // also wait on the in-flight tile gather)
+  constexpr int kQReg = kMlaDl / 32;   // 16
+  bf16x8 qf[kQReg];
   {
     const uint16_t* q = static_cast<const uint16_t*>(a.q) +
                         (static_cast<int64_t>(j) * a.n_heads + h_own) * kMlaD + grp * 8;
 #pragma unroll
-    for (int ks = 0; ks < kMlaKSteps; ++ks)
+    for (int ks = 0; ks < kQReg; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      sh.qrope[r][grp][h_own] = *reinterpret_cast<const uint4*>(q + (kQReg + r) * 32);
   }
   // O^T[c, h]: column block cb of this wave, head group hg (lane's head
   // hg*16 + li, columns 16*cb + 4*grp + 0..3 of this wave's range)
@@ -532,8 +574,11 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();         // every wave's gather landed; tile t-1 fully consumed
     asm volatile("" ::: "memory");
-    if (t + 1 < n_tiles) mla_issue_tile<1 - B, kW>(kv, sh.sidx, (t + 1) * kPipeTile, wave, lane);
     const uint8_t* tile = mla_buf<B>();
+    const bool more = t + 1 < n_tiles;
+    const int t0n = (t + 1) * kPipeTile;
+    // row index of the next gather instruction, read one k-step ahead
+    int32_t grow = (more && wave < kPipeTileInst) ? sh.sidx[t0n + mla_gather_row(wave, lane)] : 0;
     const int32_t my_row = lane < kPipeTile ? sh.sidx[t * kPipeTile + lane] : -1;
     const uint64_t valid = __ballot(my_row >= 0);
 
@@ -553,10 +598,24 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
         n0 = kfrag(0, ks + 1);
         n1 = kfrag(1, ks + 1);
       }
-      st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], st[0], 0, 0, 0);
-      st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], st[1], 0, 0, 0);
+      const bf16x8 qv = ks < kQReg ? qf[ks < kQReg ? ks : 0]
+                                   : __builtin_bit_cast(bf16x8, sh.qrope[ks - kQReg][grp][h_own]);
+      st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv, st[0], 0, 0, 0);
+      st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv, st[1], 0, 0, 0);
       k0 = n0;
       k1 = n1;
+      // the next tile's gather, one DMA instruction every four k-steps, so
+      // the vector-memory path never backs up into the MFMA stream
+      if ((ks & 3) == 1) {
+        const int i = ks >> 2;
+        const int m = wave + i * kW;
+        if (more && i < MlaIssue<kW>::kPer && m < kPipeTileInst) {
+          mla_gather_issue<1 - B>(kv, m, lane, grow);
+          const int mn = m + kW;
+          if (i + 1 < MlaIssue<kW>::kPer && mn < kPipeTileInst)
+            grow = sh.sidx[t0n + mla_gather_row(mn, lane)];
+        }
+      }
     }
     // ---- online softmax of head h_own over keys 16*kb + 4*grp + i
     float mx = -INFINITY;
@@ -595,7 +654,13 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
     psum += __shfl_xor(psum, 32);
     l_run += psum;
     sh.p[grp][h_own] = __builtin_bit_cast(uint4, pv);
-    __syncthreads();   // P and the rescale factors of every head are visible
+    // P and the rescale factors of every head visible to all waves.  Only
+    // LDS traffic is waited for: a fenced barrier would also wait for the
+    // next tile's gather that is in flight.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
     // ---- rescale this wave's columns of any head whose reference moved
     bool any = false;
@@ -611,8 +676,12 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
     }
     // ---- O^T += V^T P^T for this wave's column blocks, all heads
     bf16x8 vf[kCB];
-    const uint8_t* vbase = tile + (4 * grp + (li >> 2)) * kPipeRow + ((li & 3) >> 1) * 16 +
-                           (li & 1) * 8 + wave * kCols * 2;
+    // one integer offset, so every read below is a single step from the
+    // buffer's base: the compiler then still knows which of the two buffers
+    // it reads and does not wait for the gather in flight into the other
+    const int voff = (4 * grp + (li >> 2)) * kPipeRow + ((li & 3) >> 1) * 16 + (li & 1) * 8 +
+                     wave * kCols * 2;
+    const uint8_t* vbase = tile + voff;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       if constexpr (kTrV) {
@@ -620,7 +689,6 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
             (__attribute__((address_space(3))) i16x4*)(vbase + cb * 32));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(vbase + 16 * kPipeRow + cb * 32));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
         vf[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       } else {
         const int col = wave * kCols + cb * 16 + li;
