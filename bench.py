@@ -170,6 +170,42 @@ def decode_step(wl, ds, st, tm):
     tm.run("sparse_mla", lambda: ds.sparse_mla_decode(st["q"], st["kv"], st["topk_idx"], wl.scale, wl.d_latent, kv_scale=st["kv_scale"], out=st["out"], lse=st["lse"], workspace=st["ws"]))
 
 
+# source files whose kernels each call launches (a counter record is used only
+# while these files are unchanged since the counters were taken)
+CALL_SOURCES = {"sparse_mla": ("sparse_mla.hip", "common.h"),
+                "indexer_scores": ("indexer.hip", "common.h"),
+                "topk_select": ("topk.hip", "common.h")}
+
+
+def counted_traffic(call, workload):
+    """HBM bytes per launch of `call` from the committed rocprofv3 counter
+    record of this workload (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the counter reads for the latent-KV rerange, a copy of known size).
+    None when there is no record or the kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.txt")
+    if call not in CALL_SOURCES or not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in CALL_SOURCES[call]:
+        with open(os.path.join(ROOT, "deepseek_v3_context_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()[:16]
+    scale, rec = None, None
+    with open(path) as fh:
+        for line in fh:
+            tok = line.split()
+            if not tok or tok[0].startswith("#"):
+                continue
+            if tok[0] == "scale":
+                scale = (float(tok[1]), float(tok[2]))
+            elif tok[0] == call:
+                rec = tok
+    if scale is None or rec is None or rec[1] != sha:
+        return None
+    return int(round((float(rec[2]) * scale[0] + float(rec[3]) * scale[1]) * 1024))
+
+
 def work_model(wl, kv_len):
     """Algorithmic work per call: causal pairs for the indexer, valid top-k
     pairs for MLA; bytes are the unavoidable HBM traffic of each call."""
@@ -295,12 +331,12 @@ def main():
         ach = dw["flops"] / (d_ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+                "traffic": counted_traffic(dom, wl.name)}
     else:
         ach = dw["bytes"] / (d_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": None}
+                "traffic": counted_traffic(dom, wl.name)}
     n = st["n"]
     ms_step = elapsed / args.steps * 1e3
     line = {
