@@ -391,20 +391,26 @@ mla_mfma_kernel(MlaArgs a, int32_t keys_per_split) {
 }
 
 // ------------------------------------------------- bf16 KV, pipelined
-// One workgroup of kW = n_heads/16 waves per (query, split of its rows).
-//   * QK + softmax: wave w owns heads [16w, 16w+16).  S^T = K Q^T on
-//     v_mfma_f32_16x16x32_bf16 with K from LDS and Q^T (72 VGPRs) in
-//     registers; the online softmax of a head lives in the lane group that
-//     owns it.  The bf16 softmax weights P of every head go to LDS.
-//   * PV: wave w owns output columns [w*512/kW, (w+1)*512/kW) for ALL heads:
-//     O^T[c, h] += V^T[c, key] P^T[key, h], so each V fragment (LDS
-//     transpose read) feeds kW MFMAs and each P fragment 512/kW/16.  O^T
-//     is 128 fp32 accumulator registers per lane whatever kW is.
-// 32-row tiles are gathered straight into LDS (global_load_lds_dwordx4,
-// no VGPRs), double-buffered so the gather of tile t+1 overlaps tile t.
+// One workgroup of 2*kG waves (kG = n_heads/32) per (query, split of its
+// rows), in two groups of kG waves; group g owns heads [g*H/2, (g+1)*H/2).
+//   * QK + softmax: wave wg of group g owns 16 heads, g*H/2 + 16*wg + 0..15.
+//     S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K from LDS and Q^T (72
+//     VGPRs) in registers; the online softmax of a head lives in the lane
+//     group that owns it.  The bf16 softmax weights P go to LDS.
+//   * PV: wave wg owns output columns [wg*512/kG, (wg+1)*512/kG) of its
+//     group's heads: O^T[c, h] += V^T[c, key] P^T[key, h], so each V
+//     fragment (LDS transpose read) feeds kG MFMAs.  O^T is 128 fp32
+//     registers per lane.
+//   * Ping-pong: group 1 runs one phase behind group 0 (an extra barrier
+//     before its loop), so while one group does QK + softmax of tile t (LDS
+//     reads of K, exp on the vector ALU) the other does PV of its previous
+//     tile (MFMA-dense) on the same SIMDs.  Each tile lives in LDS for three
+//     phases, so tiles are triple-buffered.
+// 32-row tiles are gathered straight into LDS (global_load_lds_dwordx4, no
+// VGPRs) by group 0 during its PV phase, two tiles ahead.
 // Lazy rescaling: a head's reference max moves only when a tile raises it
 // by more than 2^kRescaleLog2; the owner publishes the factor and every
-// wave rescales its columns of that head.
+// wave of the group rescales its columns of that head.
 constexpr int kPipeTile = 32;                                     // rows per tile
 // Padded LDS row of the pipelined kernel: 1184 bytes (74 chunks).  With
 // this stride both the K-fragment reads (16 rows, one chunk) and the V
@@ -417,37 +423,50 @@ constexpr int kPipeTileChunks = kPipeTile * kDmaRowChunks;        // 2368
 constexpr int kPipeTileInst = kPipeTileChunks / kWave;            // 37
 constexpr int kMlaMaxKeys = 2048;
 
-__shared__ __align__(16) uint8_t g_mla_buf0[kPipeTile * kPipeRow];
-__shared__ __align__(16) uint8_t g_mla_buf1[kPipeTile * kPipeRow];
+// Three tile buffers.  The gathers into them are issued as instructions the
+// compiler does not see (mla_gather_issue), so it inserts no wait for them
+// before reading a buffer; the kernel waits for its gathers itself (vmcnt
+// before the barrier that opens a tile).
+constexpr int kPipeTileBytes = kPipeTile * kPipeRow;              // 37888
+__shared__ __align__(16) uint8_t g_mla_bufs[3 * kPipeTileBytes];
 
-template <int B>
-__device__ __forceinline__ uint8_t* mla_buf() {
-  return B ? g_mla_buf1 : g_mla_buf0;
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
+
+// DMA wave-instructions per gathering wave and tile, when kG waves gather
+// (every gathering wave issues the same count, so one vmcnt threshold
+// covers "all but the newest tile").
+template <int kG>
+struct MlaIssue {
+  static constexpr int kPer = (kPipeTileInst + kG - 1) / kG;
+};
+constexpr int kMlaIssueMax = kPipeTileInst;
+
+// DMA wave-instruction slot i of gathering wave wg: instruction m = wg +
+// i*kG of the tile, or, past the last instruction, a repeat of the same
+// wave's previous one (identical bytes to the same place).
+template <int kG>
+__device__ __forceinline__ int mla_gather_inst(int wg, int i) {
+  const int m = wg + i * kG;
+  return m < kPipeTileInst ? m : m - kG;
 }
 
-// DMA wave-instructions per wave and tile for kW waves (at most 19, for
-// two waves).
-template <int kW>
-struct MlaIssue {
-  static constexpr int kPer = (kPipeTileInst + kW - 1) / kW;
-};
-constexpr int kMlaIssueMax = (kPipeTileInst + 1) / 2;
-
-// One DMA wave-instruction of a tile gather: instruction m of the tile
-// fills LDS chunks [64m, 64m+64); lane l's chunk is row (64m+l)/74, column
-// (64m+l)%74 (columns 72, 73 are padding and re-read column 71).  The lane
-// id is made opaque so this per-lane arithmetic is recomputed at every
-// call instead of being hoisted out of the tile loop: hoisted values get
-// spilled, and a scratch reload between two DMA instructions would wait
-// for the earlier gather (vmcnt counts both).
+// One DMA wave-instruction of a tile gather: instruction m fills LDS
+// chunks [64m, 64m+64); lane l's chunk is row (64m+l)/74, column
+// (64m+l)%74 (columns 72, 73 are padding and re-read column 71).  Empty
+// slots (-1) read row 0: their logits are masked and their softmax weight
+// is 0.  The lane id is made opaque so this per-lane arithmetic is
+// recomputed at every call instead of being hoisted out of the tile loop:
+// hoisted values get spilled, and a scratch reload between two DMA
+// instructions would wait for the earlier gather (vmcnt counts both).
 __device__ __forceinline__ int mla_gather_row(int m, int lane) {
   int ln = lane;
   asm volatile("" : "+v"(ln));
   return (m * kWave + ln) / kDmaRowChunks;
 }
 
-template <int B>
-__device__ __forceinline__ void mla_gather_issue(const uint8_t* kv, int m, int lane,
+__device__ __forceinline__ void mla_gather_issue(const uint8_t* kv, uint8_t* buf, int m, int lane,
                                                  int32_t row) {
   int ln = lane;
   asm volatile("" : "+v"(ln));
@@ -455,60 +474,67 @@ __device__ __forceinline__ void mla_gather_issue(const uint8_t* kv, int m, int l
   const int c = P - (P / kDmaRowChunks) * kDmaRowChunks;
   const int cc = c < kMlaRowChunks ? c : kMlaRowChunks - 1;
   row = row < 0 ? 0 : row;
-  __builtin_amdgcn_global_load_lds(
-      kv + static_cast<int64_t>(row) * kMlaRowBytes + cc * 16,
-      (__attribute__((address_space(3))) void*)(mla_buf<B>() + m * kWave * 16), 16, 0, 0);
+  const uint8_t* src = kv + static_cast<int64_t>(row) * kMlaRowBytes + cc * 16;
+  // LDS destination of lane l: M0 + 16*l (M0 = this instruction's chunk
+  // block, the same for the whole wave); one wait state between writing M0
+  // and the instruction that reads it
+  const uint32_t dst = static_cast<uint32_t>(
+      (size_t)((__attribute__((address_space(3))) uint8_t*)(buf + m * kWave * 16)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(dst))
+               : "memory", "m0");
 }
 
-// Gathers a whole tile (rows sidx[t0 .. t0+31]) into buffer B.  Wave-
-// instruction m fills LDS chunks [64m, 64m+64) of the padded tile; lane l's
-// chunk is row (64m+l)/74, column (64m+l)%74 (columns 72, 73 are padding
-// and re-read column 71).  Empty slots (-1) read row 0: their logits are
-// masked and their softmax weight is 0.
-template <int B, int kW>
-__device__ __forceinline__ void mla_issue_tile(const uint8_t* kv, const int32_t* sidx, int t0,
-                                               int wave, int lane) {
+// Gathers a whole tile (rows sidx[t0 .. t0+31]) into buf: this wave's kPer
+// instructions, row indices read first (one LDS round trip).
+template <int kG>
+__device__ __forceinline__ void mla_issue_tile(const uint8_t* kv, uint8_t* buf, const int32_t* sidx,
+                                               int t0, int wg, int lane) {
+  constexpr int kPer = MlaIssue<kG>::kPer;
   int32_t row[kMlaIssueMax];
 #pragma unroll
-  for (int i = 0; i < MlaIssue<kW>::kPer; ++i) {
-    const int m = wave + i * kW;
-    row[i] = m < kPipeTileInst ? sidx[t0 + mla_gather_row(m, lane)] : 0;
-  }
+  for (int i = 0; i < kPer; ++i) row[i] = sidx[t0 + mla_gather_row(mla_gather_inst<kG>(wg, i), lane)];
 #pragma unroll
-  for (int i = 0; i < MlaIssue<kW>::kPer; ++i) {
-    const int m = wave + i * kW;
-    if (m < kPipeTileInst) mla_gather_issue<B>(kv, m, lane, row[i]);
-  }
+  for (int i = 0; i < kPer; ++i) mla_gather_issue(kv, buf, mla_gather_inst<kG>(wg, i), lane, row[i]);
 }
 
-template <int kW>
+template <int kG>
 struct MlaShared {
-  static constexpr int kHeads = 16 * kW;
+  static constexpr int kHeads = 32 * kG;
+  static constexpr int kHalf = 16 * kG;   // heads per group
   uint4 qrope[2][4][kHeads];   // rope k-steps of Q^T: [ks-16][lane group][head]
   int32_t sidx[kMlaMaxKeys];
-  uint4 p[4][kHeads];          // P^T fragments: [lane group][head] -> 8 bf16
-  float alpha[kHeads];         // per-tile rescale factor of each head
-  int32_t rescale[kW];         // wave w raised a reference max this tile
-  int32_t wave_cnt[kW];        // index compaction scratch
+  uint4 p[2][4][kHalf];        // P^T fragments: [group][lane group][head in group]
+  float alpha[2][kHalf];       // per-tile rescale factor of each head
+  int32_t rescale[2][kG];      // wave wg of group g raised a reference max
+  int32_t wave_cnt[2 * kG];    // index compaction scratch
   float m_fin[kHeads], l_fin[kHeads];
 };
 
-template <bool kTrV, int kW>
-__global__ void __launch_bounds__(kWave * kW)
+template <bool kTrV, int kG>
+__global__ void __launch_bounds__(kWave * 2 * kG)
 mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
+  constexpr int kW = 2 * kG;
   constexpr int kThreads = kWave * kW;
-  constexpr int kCols = kMlaDl / kW;          // output columns per wave
+  constexpr int kHalf = 16 * kG;              // heads per group
+  constexpr int kCols = kMlaDl / kG;          // output columns per wave
   constexpr int kCB = kCols / 16;             // 16-column blocks per wave
-  __shared__ MlaShared<kW> sh;
+  constexpr int kCBC = kCB < 4 ? kCB : 4;     // column blocks per PV chunk
+  constexpr int kPer = MlaIssue<kG>::kPer;    // DMA wave-instructions per tile
+  __shared__ MlaShared<kG> sh;
 
   const int32_t j = blockIdx.x / a.n_splits;
   const int32_t split = blockIdx.x - j * a.n_splits;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave / kG;                    // group
+  const int wg = wave - g * kG;               // wave within the group
   const int grp = lane >> 4;
   const int li = lane & 15;
-  const int h_own = wave * 16 + li;           // head whose softmax this lane keeps
+  const int hq = wg * 16 + li;                // head (within the group) this lane keeps
+  const int h_own = g * kHalf + hq;
 
   const int32_t s_begin = split * keys_per_split;
   int32_t s_end = s_begin + keys_per_split;
@@ -542,7 +568,7 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
   // Q^T fragments (B operand of QK): head h_own, dims 32*ks + 8*grp + 0..7;
   // the 16 latent k-steps stay in VGPRs, the 2 rope k-steps in LDS (this
   // keeps the wave clear of register spills, whose scratch reloads would
-  // also wait on the in-flight tile gather)
+  // also wait on the in-flight tile gathers)
   constexpr int kQReg = kMlaDl / 32;   // 16
   bf16x8 qf[kQReg];
   {
@@ -555,40 +581,52 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
     for (int r = 0; r < 2; ++r)
       sh.qrope[r][grp][h_own] = *reinterpret_cast<const uint4*>(q + (kQReg + r) * 32);
   }
-  // O^T[c, h]: column block cb of this wave, head group hg (lane's head
-  // hg*16 + li, columns 16*cb + 4*grp + 0..3 of this wave's range)
-  f32x4 o[kCB][kW];
+  // O^T[c, h]: column block cb of this wave, head block hg of the group
+  // (head g*H/2 + hg*16 + li, columns 16*cb + 4*grp + 0..3 of this wave's
+  // range)
+  f32x4 o[kCB][kG];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-    for (int hg = 0; hg < kW; ++hg) o[cb][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hg = 0; hg < kG; ++hg) o[cb][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;
   const float scale2 = a.sm_scale * kLog2e;
   const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
-  __syncthreads();   // sidx ready; no gather in flight yet
-  if (n_tiles > 0) mla_issue_tile<0, kW>(kv, sh.sidx, 0, wave, lane);
+  // Q loads complete here, before any gather is in flight: a wait for them
+  // inside the tile loop would also wait for the gathers
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();   // sidx and rope ready
+  if (g == 0) {
+    if (n_tiles > 0) mla_issue_tile<kG>(kv, g_mla_bufs, sh.sidx, 0, wg, lane);
+    if (n_tiles > 1) mla_issue_tile<kG>(kv, g_mla_bufs + kPipeTileBytes, sh.sidx, kPipeTile, wg, lane);
+  }
+  if (g == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind
 
-  auto step = [&](auto bufc, int t) {
-    constexpr int B = decltype(bufc)::value;
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gather of tile t landed
+  // tile t lives in buffer t mod 3
+  for (int32_t t = 0, b = 0; t < n_tiles; ++t, b = b == 2 ? 0 : b + 1) {
+    const int bn = b == 0 ? 2 : b - 1;    // buffer of tile t+2 (= that of t-1)
+    // this wave's gather of tile t landed (tile t+1 may still be in flight)
+    if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();         // every wave's gather landed; tile t-1 fully consumed
+    __builtin_amdgcn_s_barrier();         // tile t complete for every wave
     asm volatile("" ::: "memory");
-    const uint8_t* tile = mla_buf<B>();
-    const bool more = t + 1 < n_tiles;
-    const int t0n = (t + 1) * kPipeTile;
-    // row index of the next gather instruction, read one k-step ahead
-    int32_t grow = (more && wave < kPipeTileInst) ? sh.sidx[t0n + mla_gather_row(wave, lane)] : 0;
+    const uint8_t* tile = g_mla_bufs + b * kPipeTileBytes;
+    // per-lane offsets recomputed every tile from an opaque copy of the lane
+    // id: hoisted out of the loop they would be spilled
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int li_t = ln & 15, grp_t = ln >> 4;
     const int32_t my_row = lane < kPipeTile ? sh.sidx[t * kPipeTile + lane] : -1;
     const uint64_t valid = __ballot(my_row >= 0);
 
     // ---- S^T = K Q^T for this wave's 16 heads: 2 blocks of 16 keys; the
     //      fragments of k-step ks+1 are read while ks is multiplied
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const uint8_t* kbase = tile + li * kPipeRow + grp * 16;
+    const int koff = li_t * kPipeRow + grp_t * 16;
     auto kfrag = [&](int kb, int ks) {
       return __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(kbase + kb * 16 * kPipeRow + ks * 64));
+          bf16x8, *reinterpret_cast<const uint4*>(tile + koff + kb * 16 * kPipeRow + ks * 64));
     };
     bf16x8 k0 = kfrag(0, 0), k1 = kfrag(1, 0);
 #pragma unroll
@@ -604,18 +642,6 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
       st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv, st[1], 0, 0, 0);
       k0 = n0;
       k1 = n1;
-      // the next tile's gather, one DMA instruction every four k-steps, so
-      // the vector-memory path never backs up into the MFMA stream
-      if ((ks & 3) == 1) {
-        const int i = ks >> 2;
-        const int m = wave + i * kW;
-        if (more && i < MlaIssue<kW>::kPer && m < kPipeTileInst) {
-          mla_gather_issue<1 - B>(kv, m, lane, grow);
-          const int mn = m + kW;
-          if (i + 1 < MlaIssue<kW>::kPer && mn < kPipeTileInst)
-            grow = sh.sidx[t0n + mla_gather_row(mn, lane)];
-        }
-      }
     }
     // ---- online softmax of head h_own over keys 16*kb + 4*grp + i
     float mx = -INFINITY;
@@ -638,8 +664,8 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
       l_run *= alpha;
     }
     const bool wave_rescales = __ballot(need) != 0ull;
-    if (lane < 16) sh.alpha[h_own] = alpha;
-    if (lane == 0) sh.rescale[wave] = wave_rescales;
+    if (lane < 16) sh.alpha[g][hq] = alpha;
+    if (lane == 0) sh.rescale[g][wg] = wave_rescales;
     float psum = 0.f;
     bf16x8 pv;
 #pragma unroll
@@ -653,10 +679,10 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
     l_run += psum;
-    sh.p[grp][h_own] = __builtin_bit_cast(uint4, pv);
-    // P and the rescale factors of every head visible to all waves.  Only
-    // LDS traffic is waited for: a fenced barrier would also wait for the
-    // next tile's gather that is in flight.
+    sh.p[g][grp][hq] = __builtin_bit_cast(uint4, pv);
+    // P and the rescale factors of the group visible to all its waves.
+    // Only LDS traffic is waited for: a fenced barrier would also wait for
+    // the tile gathers in flight.
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -665,56 +691,72 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
     // ---- rescale this wave's columns of any head whose reference moved
     bool any = false;
 #pragma unroll
-    for (int w = 0; w < kW; ++w) any |= sh.rescale[w] != 0;
+    for (int w = 0; w < kG; ++w) any |= sh.rescale[g][w] != 0;
     if (any) {
 #pragma unroll
-      for (int hg = 0; hg < kW; ++hg) {
-        const float al = sh.alpha[hg * 16 + li];
+      for (int hg = 0; hg < kG; ++hg) {
+        const float al = sh.alpha[g][hg * 16 + li];
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) o[cb][hg] *= al;
       }
     }
-    // ---- O^T += V^T P^T for this wave's column blocks, all heads
-    bf16x8 vf[kCB];
-    // one integer offset, so every read below is a single step from the
-    // buffer's base: the compiler then still knows which of the two buffers
-    // it reads and does not wait for the gather in flight into the other
-    const int voff = (4 * grp + (li >> 2)) * kPipeRow + ((li & 3) >> 1) * 16 + (li & 1) * 8 +
-                     wave * kCols * 2;
-    const uint8_t* vbase = tile + voff;
+    // ---- O^T += V^T P^T for this wave's column blocks, the group's heads;
+    //      group 0 also gathers tile t+2 (into the buffer of tile t-1, which
+    //      both groups have finished with) spread over the products
+    const bool gather = g == 0 && t + 2 < n_tiles;
+    const int t0n = (t + 2) * kPipeTile;
+    int32_t grow = gather ? sh.sidx[t0n + mla_gather_row(mla_gather_inst<kG>(wg, 0), lane)] : 0;
+    const int voff = (4 * grp_t + (li_t >> 2)) * kPipeRow + ((li_t & 3) >> 1) * 16 +
+                     (li_t & 1) * 8 + wg * kCols * 2;
+    // column blocks in chunks of kCBC: the chunk's V^T fragments stay in
+    // registers while every head block of P multiplies them
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      if constexpr (kTrV) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vbase + cb * 32));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vbase + 16 * kPipeRow + cb * 32));
-        vf[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      } else {
-        const int col = wave * kCols + cb * 16 + li;
-        const uint8_t* p0 = tile + 4 * grp * kPipeRow + (col >> 3) * 16 + (col & 7) * 2;
+    for (int c0 = 0; c0 < kCB; c0 += kCBC) {
+      bf16x8 vf[kCBC];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vf[cb][i] = *reinterpret_cast<const __bf16*>(p0 + i * kPipeRow);
-          vf[cb][4 + i] = *reinterpret_cast<const __bf16*>(p0 + (16 + i) * kPipeRow);
+      for (int c = 0; c < kCBC; ++c) {
+        const int cb = c0 + c;
+        if constexpr (kTrV) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tile + voff + cb * 32));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tile + voff + 16 * kPipeRow + cb * 32));
+          vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          const int col = wg * kCols + cb * 16 + li;
+          const uint8_t* p0 = tile + 4 * grp * kPipeRow + (col >> 3) * 16 + (col & 7) * 2;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vf[c][i] = *reinterpret_cast<const __bf16*>(p0 + i * kPipeRow);
+            vf[c][4 + i] = *reinterpret_cast<const __bf16*>(p0 + (16 + i) * kPipeRow);
+          }
         }
       }
-    }
-    bf16x8 pf = __builtin_bit_cast(bf16x8, sh.p[grp][li]);
+      bf16x8 pf = __builtin_bit_cast(bf16x8, sh.p[g][grp][li]);
 #pragma unroll
-    for (int hg = 0; hg < kW; ++hg) {
-      bf16x8 pn = pf;
-      if (hg + 1 < kW) pn = __builtin_bit_cast(bf16x8, sh.p[grp][(hg + 1) * 16 + li]);
+      for (int hg = 0; hg < kG; ++hg) {
+        bf16x8 pn = pf;
+        if (hg + 1 < kG) pn = __builtin_bit_cast(bf16x8, sh.p[g][grp][(hg + 1) * 16 + li]);
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb)
-        o[cb][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[cb], pf, o[cb][hg], 0, 0, 0);
-      pf = pn;
+        for (int c = 0; c < kCBC; ++c) {
+          o[c0 + c][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c], pf, o[c0 + c][hg], 0, 0, 0);
+          // DMA slot i goes after product number i * kG * kCB / kPer
+          const int prod = c0 * kG + hg * kCBC + c;
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) {
+            if (i * kG * kCB / kPer == prod && gather) {
+              mla_gather_issue(kv, g_mla_bufs + bn * kPipeTileBytes, mla_gather_inst<kG>(wg, i), lane,
+                               grow);
+              if (i + 1 < kPer)
+                grow = sh.sidx[t0n + mla_gather_row(mla_gather_inst<kG>(wg, i + 1), lane)];
+            }
+          }
+        }
+        pf = pn;
+      }
     }
-  };
-  for (int32_t t = 0; t < n_tiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1);
   }
+  if (g == 0) __builtin_amdgcn_s_barrier();   // pairs with group 1's leading barrier
 
   // ---- epilogue: owners publish (m, l); every wave writes its columns
   if (lane < 16) {
@@ -722,10 +764,10 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
     sh.l_fin[h_own] = l_run;
   }
   __syncthreads();
-  const int col0 = wave * kCols + grp * 4;
+  const int col0 = wg * kCols + grp * 4;
 #pragma unroll
-  for (int hg = 0; hg < kW; ++hg) {
-    const int h = hg * 16 + li;
+  for (int hg = 0; hg < kG; ++hg) {
+    const int h = g * kHalf + hg * 16 + li;
     const float lf = sh.l_fin[h];
     if (a.n_splits == 1) {
       const float inv = lf > 0.f ? 1.f / lf : 0.f;
@@ -852,16 +894,16 @@ ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
   if (a.kv_dtype == DS_BF16) {
     switch (a.n_heads) {
       case 32:
-        if (tr) mla_bf16_pipelined_kernel<true, 2><<<blocks, kWave * 2, 0, s>>>(a, per_split);
-        else mla_bf16_pipelined_kernel<false, 2><<<blocks, kWave * 2, 0, s>>>(a, per_split);
+        if (tr) mla_bf16_pipelined_kernel<true, 1><<<blocks, kWave * 2, 0, s>>>(a, per_split);
+        else mla_bf16_pipelined_kernel<false, 1><<<blocks, kWave * 2, 0, s>>>(a, per_split);
         break;
       case 64:
-        if (tr) mla_bf16_pipelined_kernel<true, 4><<<blocks, kWave * 4, 0, s>>>(a, per_split);
-        else mla_bf16_pipelined_kernel<false, 4><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+        if (tr) mla_bf16_pipelined_kernel<true, 2><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+        else mla_bf16_pipelined_kernel<false, 2><<<blocks, kWave * 4, 0, s>>>(a, per_split);
         break;
       default:
-        if (tr) mla_bf16_pipelined_kernel<true, 8><<<blocks, kWave * 8, 0, s>>>(a, per_split);
-        else mla_bf16_pipelined_kernel<false, 8><<<blocks, kWave * 8, 0, s>>>(a, per_split);
+        if (tr) mla_bf16_pipelined_kernel<true, 4><<<blocks, kWave * 8, 0, s>>>(a, per_split);
+        else mla_bf16_pipelined_kernel<false, 4><<<blocks, kWave * 8, 0, s>>>(a, per_split);
     }
     ds_status st = check_launch("sparse_mla");
     if (st != DS_OK || a.n_splits == 1) return st;
