@@ -434,22 +434,35 @@ __shared__ __align__(16) uint8_t g_mla_bufs[3 * kPipeTileBytes];
 // of this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
 
-// DMA wave-instructions per gathering wave and tile, when kG waves gather
-// (every gathering wave issues the same count, so one vmcnt threshold
-// covers "all but the newest tile").
-template <int kG>
+// DMA wave-instructions per wave and tile when kW waves share a tile's
+// gather (every wave issues the same count; slots past the last
+// instruction repeat the wave's previous one: identical bytes to the same
+// place).
+template <int kW>
 struct MlaIssue {
-  static constexpr int kPer = (kPipeTileInst + kG - 1) / kG;
+  static constexpr int kPer = (kPipeTileInst + kW - 1) / kW;
 };
 constexpr int kMlaIssueMax = kPipeTileInst;
 
-// DMA wave-instruction slot i of gathering wave wg: instruction m = wg +
-// i*kG of the tile, or, past the last instruction, a repeat of the same
-// wave's previous one (identical bytes to the same place).
-template <int kG>
-__device__ __forceinline__ int mla_gather_inst(int wg, int i) {
-  const int m = wg + i * kG;
-  return m < kPipeTileInst ? m : m - kG;
+template <int kW>
+__device__ __forceinline__ int mla_gather_inst(int wave, int i) {
+  const int m = wave + i * kW;
+  return m < kPipeTileInst ? m : m - kW;
+}
+
+// Cross-lane reductions over the four 16-lane rows of a wave (lanes l,
+// l^16, l^32, l^48) with the row-swap permutes: no LDS round trip.
+__device__ __forceinline__ float mla_rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float mla_rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // One DMA wave-instruction of a tile gather: instruction m fills LDS
@@ -486,17 +499,17 @@ __device__ __forceinline__ void mla_gather_issue(const uint8_t* kv, uint8_t* buf
                : "memory", "m0");
 }
 
-// Gathers a whole tile (rows sidx[t0 .. t0+31]) into buf: this wave's kPer
-// instructions, row indices read first (one LDS round trip).
-template <int kG>
+// This wave's slots of the gather of tile rows sidx[t0 .. t0+31] into buf
+// (row indices read first: one LDS round trip).
+template <int kW>
 __device__ __forceinline__ void mla_issue_tile(const uint8_t* kv, uint8_t* buf, const int32_t* sidx,
-                                               int t0, int wg, int lane) {
-  constexpr int kPer = MlaIssue<kG>::kPer;
+                                               int t0, int wave, int lane) {
+  constexpr int kPer = MlaIssue<kW>::kPer;
   int32_t row[kMlaIssueMax];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) row[i] = sidx[t0 + mla_gather_row(mla_gather_inst<kG>(wg, i), lane)];
+  for (int i = 0; i < kPer; ++i) row[i] = sidx[t0 + mla_gather_row(mla_gather_inst<kW>(wave, i), lane)];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) mla_gather_issue(kv, buf, mla_gather_inst<kG>(wg, i), lane, row[i]);
+  for (int i = 0; i < kPer; ++i) mla_gather_issue(kv, buf, mla_gather_inst<kW>(wave, i), lane, row[i]);
 }
 
 template <int kG>
@@ -521,7 +534,7 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
   constexpr int kCols = kMlaDl / kG;          // output columns per wave
   constexpr int kCB = kCols / 16;             // 16-column blocks per wave
   constexpr int kCBC = kCB < 4 ? kCB : 4;     // column blocks per PV chunk
-  constexpr int kPer = MlaIssue<kG>::kPer;    // DMA wave-instructions per tile
+  constexpr int kPer = MlaIssue<kW>::kPer;    // DMA wave-instructions per wave and tile
   __shared__ MlaShared<kG> sh;
 
   const int32_t j = blockIdx.x / a.n_splits;
@@ -596,21 +609,44 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
   // inside the tile loop would also wait for the gathers
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();   // sidx and rope ready
-  if (g == 0) {
-    if (n_tiles > 0) mla_issue_tile<kG>(kv, g_mla_bufs, sh.sidx, 0, wg, lane);
-    if (n_tiles > 1) mla_issue_tile<kG>(kv, g_mla_bufs + kPipeTileBytes, sh.sidx, kPipeTile, wg, lane);
+  // Gathers: every wave issues its slots of tile t+2 while tile t is in
+  // use (group 0 during its PV(t), group 1 during its QK(t); both into the
+  // buffer of tile t-1, which both groups have finished with by then), and
+  // waits for its slots of a tile before the barrier after which group 0
+  // opens it (group 0: the tile-opening barrier; group 1, one phase
+  // behind: the P barrier of the step before).  Here: tiles 0 and 1.
+  if (n_tiles > 0) mla_issue_tile<kW>(kv, g_mla_bufs, sh.sidx, 0, wave, lane);
+  if (n_tiles > 1) mla_issue_tile<kW>(kv, g_mla_bufs + kPipeTileBytes, sh.sidx, kPipeTile, wave, lane);
+  if (g == 1) {
+    // group 1 runs one phase behind; its part of tile 0 lands before
+    // group 0 opens it
+    if (n_tiles > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
-  if (g == 1) __builtin_amdgcn_s_barrier();   // group 1 runs one phase behind
 
   // tile t lives in buffer t mod 3
   for (int32_t t = 0, b = 0; t < n_tiles; ++t, b = b == 2 ? 0 : b + 1) {
-    const int bn = b == 0 ? 2 : b - 1;    // buffer of tile t+2 (= that of t-1)
     // this wave's gather of tile t landed (tile t+1 may still be in flight)
-    if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (g == 0) {
+      // group 0's slots of tile t landed (those of tile t+1 may be in flight)
+      if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();         // tile t complete for every wave
     asm volatile("" ::: "memory");
+    // QK and softmax are this SIMD's critical path: issue ahead of the
+    // other group's PV products
+    __builtin_amdgcn_s_setprio(2);
+    // tile t+2 goes into the buffer of tile t-1
+    const bool gather = t + 2 < n_tiles;
+    uint8_t* gbuf = g_mla_bufs + (b == 0 ? 2 : b - 1) * kPipeTileBytes;
+    const int t0g = (t + 2) * kPipeTile;
+    // row index of this wave's next gather slot, read one slot ahead
+    int32_t grow = (g == 1 && gather) ? sh.sidx[t0g + mla_gather_row(mla_gather_inst<kW>(wave, 0), lane)] : 0;
     const uint8_t* tile = g_mla_bufs + b * kPipeTileBytes;
     // per-lane offsets recomputed every tile from an opaque copy of the lane
     // id: hoisted out of the loop they would be spilled
@@ -642,6 +678,14 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
       st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv, st[1], 0, 0, 0);
       k0 = n0;
       k1 = n1;
+      // group 1: this wave's gather slots of tile t+2, spread over the k-steps
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (i * kMlaKSteps / kPer == ks && g == 1 && gather) {
+          mla_gather_issue(kv, gbuf, mla_gather_inst<kW>(wave, i), lane, grow);
+          if (i + 1 < kPer) grow = sh.sidx[t0g + mla_gather_row(mla_gather_inst<kW>(wave, i + 1), lane)];
+        }
+      }
     }
     // ---- online softmax of head h_own over keys 16*kb + 4*grp + i
     float mx = -INFINITY;
@@ -654,8 +698,7 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
         st[kb][i] = l;
         mx = fmaxf(mx, l);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = mla_rows_max(mx);
     const bool need = mx > m_ref + kRescaleLog2;
     float alpha = 1.f;
     if (need) {
@@ -676,17 +719,25 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
         psum += pw;
         pv[kb * 4 + i] = static_cast<__bf16>(pw);
       }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = mla_rows_sum(psum);
     l_run += psum;
     sh.p[g][grp][hq] = __builtin_bit_cast(uint4, pv);
     // P and the rescale factors of the group visible to all its waves.
     // Only LDS traffic is waited for: a fenced barrier would also wait for
     // the tile gathers in flight.
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    if (g == 1) {
+      // group 1's slots of tile t+1 landed before group 0 opens it after
+      // this barrier (those of tile t+2 may be in flight)
+      if (gather) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_setprio(0);
+    // group 0: its gather slots of tile t+2 go out spread over the products
+    if (g == 0 && gather) grow = sh.sidx[t0g + mla_gather_row(mla_gather_inst<kW>(wave, 0), lane)];
 
     // ---- rescale this wave's columns of any head whose reference moved
     bool any = false;
@@ -700,12 +751,7 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
         for (int cb = 0; cb < kCB; ++cb) o[cb][hg] *= al;
       }
     }
-    // ---- O^T += V^T P^T for this wave's column blocks, the group's heads;
-    //      group 0 also gathers tile t+2 (into the buffer of tile t-1, which
-    //      both groups have finished with) spread over the products
-    const bool gather = g == 0 && t + 2 < n_tiles;
-    const int t0n = (t + 2) * kPipeTile;
-    int32_t grow = gather ? sh.sidx[t0n + mla_gather_row(mla_gather_inst<kG>(wg, 0), lane)] : 0;
+    // ---- O^T += V^T P^T for this wave's column blocks, the group's heads
     const int voff = (4 * grp_t + (li_t >> 2)) * kPipeRow + ((li_t & 3) >> 1) * 16 +
                      (li_t & 1) * 8 + wg * kCols * 2;
     // column blocks in chunks of kCBC: the chunk's V^T fragments stay in
@@ -740,15 +786,13 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
 #pragma unroll
         for (int c = 0; c < kCBC; ++c) {
           o[c0 + c][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c], pf, o[c0 + c][hg], 0, 0, 0);
-          // DMA slot i goes after product number i * kG * kCB / kPer
           const int prod = c0 * kG + hg * kCBC + c;
 #pragma unroll
           for (int i = 0; i < kPer; ++i) {
-            if (i * kG * kCB / kPer == prod && gather) {
-              mla_gather_issue(kv, g_mla_bufs + bn * kPipeTileBytes, mla_gather_inst<kG>(wg, i), lane,
-                               grow);
+            if (i * kG * kCB / kPer == prod && g == 0 && gather) {
+              mla_gather_issue(kv, gbuf, mla_gather_inst<kW>(wave, i), lane, grow);
               if (i + 1 < kPer)
-                grow = sh.sidx[t0n + mla_gather_row(mla_gather_inst<kG>(wg, i + 1), lane)];
+                grow = sh.sidx[t0g + mla_gather_row(mla_gather_inst<kW>(wave, i + 1), lane)];
             }
           }
         }
