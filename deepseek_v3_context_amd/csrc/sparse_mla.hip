@@ -859,6 +859,455 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
   }
 }
 
+// ------------------------------------------- bf16 KV, 32 heads per wave
+// One workgroup of kNW = n_heads/32 waves (one per SIMD) per (query, split
+// of its rows).  Wave w computes S^T for 32 heads (two 16-head MFMA blocks
+// share every K fragment read from LDS, so the LDS read traffic of QK is
+// half that of 16 heads per wave, the bound of that form), and PV for
+// output columns [w*512/kNW, (w+1)*512/kNW) of every head: O^T is (512/kNW)
+// x 32kNW / 64 lanes = 256 fp32 per lane, held in the accumulator
+// registers (one wave per SIMD has 512), next to the 128 VGPRs of Q^T.
+//
+// Softmax reference: the logits of a head are taken relative to its
+// maximum over the first tile and never rescaled afterwards (so the
+// accumulators are only ever touched by MFMA).  A later tile whose maximum
+// exceeds the reference by more than 2^kWideBail (weights up to 2^64 are
+// exact in fp32/bf16 range terms) makes the workgroup start over with the
+// exact maximum from a first pass over all its rows.
+constexpr float kWideBail = 64.f;
+
+// QK products with the accumulator in VGPRs (the compiler gives every MFMA
+// of a function the same accumulator file, and O^T fills the accumulator
+// registers): dst = srcC (exact overlap; the hardware forwards the
+// accumulation chain).  Results are read only after mla_qk_settle.
+__device__ __forceinline__ f32x4 mla_qk_first(bf16x8 k, bf16x8 q) {
+  f32x4 d;
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(k), "v"(q));
+  return d;
+}
+__device__ __forceinline__ void mla_qk_acc(f32x4& d, bf16x8 k, bf16x8 q) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "v"(q));
+}
+// Wait states between the last QK product and the first vector-ALU read of
+// its result (the compiler does not see inside the instructions above):
+// 24 >= the XDL-write-to-VALU-read requirement of an 8-pass MFMA.
+__device__ __forceinline__ void mla_qk_settle(f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// Gather slots of the wide kernel with the address arithmetic taken out of
+// the tile loop: for each of this wave's slots, the lane's row slot in the
+// tile and byte column are packed into 16 bits (row << 11 | column), two
+// slots per register, computed once.  A slot is then one LDS read of the
+// row index, one multiply-add and the DMA instruction (SGPR base + 32-bit
+// offset: the latent KV must be smaller than 4 GiB).  One wave per SIMD
+// issues in order, so every instruction here delays its MFMAs.
+template <int kNW>
+struct WideGather {
+  static constexpr int kPer = MlaIssue<kNW>::kPer;
+  uint32_t info[(kPer + 1) / 2];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPer; i += 2) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (i + h < kPer) {
+          const int P = mla_gather_inst<kNW>(wave, i + h) * kWave + lane;
+          const int r = P / kDmaRowChunks;
+          const int c = P - r * kDmaRowChunks;
+          const uint32_t e = (static_cast<uint32_t>(r) << 11) |
+                             static_cast<uint32_t>((c < kMlaRowChunks ? c : kMlaRowChunks - 1) * 16);
+          v |= e << (16 * h);
+        }
+      }
+      info[i / 2] = v;
+    }
+  }
+  __device__ __forceinline__ int row_slot(int i) const { return (info[i / 2] >> (16 * (i & 1) + 11)) & 31; }
+  __device__ __forceinline__ uint32_t col(int i) const { return (info[i / 2] >> (16 * (i & 1))) & 2047; }
+};
+
+// One DMA wave-instruction: 16 bytes of row `row` at byte column colb to
+// LDS address lds + 16*lane (lds: the instruction's chunk block in a tile
+// buffer, the same for the whole wave).
+__device__ __forceinline__ void wide_gather_issue(const uint8_t* kv, uint32_t lds, int32_t row,
+                                                  uint32_t colb) {
+  row = row < 0 ? 0 : row;
+  const uint32_t off = static_cast<uint32_t>(row) * kMlaRowBytes + colb;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(kv), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int kNW>
+struct MlaWideShared {
+  static constexpr int kHeads = 32 * kNW;
+  uint4 qrope[2][4][kHeads];   // rope k-steps of Q^T: [ks-16][lane group][head]
+  int32_t sidx[kMlaMaxKeys];
+  uint4 p[4][kHeads];          // P^T fragments: [lane group][head] -> 8 bf16
+  int32_t wave_cnt[kNW];       // index compaction scratch
+  int32_t bail[kNW];           // wave w saw a tile beyond its reference + 2^kWideBail
+  float m_fin[kHeads], l_fin[kHeads];
+};
+
+template <bool kTrV, int kNW>
+__global__ void __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
+  constexpr int kThreads = kWave * kNW;
+  constexpr int kHeads = 32 * kNW;
+  constexpr int kHG = kHeads / 16;            // 16-head blocks of PV
+  constexpr int kCols = kMlaDl / kNW;         // output columns per wave
+  constexpr int kCB = kCols / 16;             // 16-column blocks per wave
+  constexpr int kCBC = kCB < 4 ? kCB : 4;     // column blocks per PV chunk
+  constexpr int kPer = MlaIssue<kNW>::kPer;   // DMA wave-instructions per wave and tile
+  constexpr int kQReg = kMlaDl / 32;          // latent k-steps of Q^T in VGPRs (16)
+  __shared__ MlaWideShared<kNW> sh;
+  // Names an accumulator register so that the compiler places the MFMA
+  // accumulators (O^T) in the accumulator file.
+  asm volatile("" ::: "a0");
+
+  const int32_t j = blockIdx.x / a.n_splits;
+  const int32_t split = blockIdx.x - j * a.n_splits;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4;
+  const int li = lane & 15;
+  const int h0 = wave * 32 + li;              // heads h0, h0+16: logits and softmax of this lane
+
+  const int32_t s_begin = split * keys_per_split;
+  int32_t s_end = s_begin + keys_per_split;
+  s_end = s_end < a.topk ? s_end : a.topk;
+  const int32_t n_keys = s_end > s_begin ? s_end - s_begin : 0;
+  // valid row indices, compacted in their given order (ordered ballot scan)
+  const int32_t* idx_row = a.topk_idx + static_cast<int64_t>(j) * a.topk + s_begin;
+  int32_t n_valid = 0;
+  for (int32_t i0 = 0; i0 < n_keys; i0 += kThreads) {
+    const int32_t i = i0 + tid;
+    const int32_t r = i < n_keys ? idx_row[i] : -1;
+    const bool ok = r >= 0 && r < a.kv_rows;
+    const uint64_t ball = __ballot(ok);
+    if (lane == 0) sh.wave_cnt[wave] = static_cast<int32_t>(__popcll(ball));
+    __syncthreads();
+    int32_t before = n_valid, total = 0;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      const int32_t c = sh.wave_cnt[w];
+      before += w < wave ? c : 0;
+      total += c;
+    }
+    if (ok) sh.sidx[before + __popcll(ball & ((1ull << lane) - 1ull))] = r;
+    n_valid += total;
+    __syncthreads();
+  }
+  const int32_t n_tiles = static_cast<int32_t>(ceil_div(n_valid, kPipeTile));
+  for (int32_t i = n_valid + tid; i < n_tiles * kPipeTile; i += kThreads) sh.sidx[i] = -1;
+  if (tid < kNW) sh.bail[tid] = 0;
+
+  // Q^T fragments (B operand of QK) of heads h0 and h0+16: dims 32*ks +
+  // 8*grp + 0..7; the latent k-steps in VGPRs, the 2 rope k-steps in LDS
+  bf16x8 qf[2][kQReg];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
+                        (static_cast<int64_t>(j) * a.n_heads + h0 + 16 * hb) * kMlaD + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < kQReg; ++ks)
+      qf[hb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      sh.qrope[r][grp][h0 + 16 * hb] = *reinterpret_cast<const uint4*>(q + (kQReg + r) * 32);
+  }
+  const float scale2 = a.sm_scale * kLog2e;
+  const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
+  const uint32_t lds_bufs = static_cast<uint32_t>(
+      (size_t)((__attribute__((address_space(3))) uint8_t*)g_mla_bufs));
+  WideGather<kNW> gs;
+  gs.init(wave, lane);
+  // LDS address of slot i's chunk block in buffer b
+  auto slot_lds = [&](int b, int i) {
+    return lds_bufs + static_cast<uint32_t>(b * kPipeTileBytes + mla_gather_inst<kNW>(wave, i) * kWave * 16);
+  };
+  // all of this wave's slots of the tile with rows sidx[t0..] into buffer b
+  auto issue_tile = [&](int b, int t0) {
+    int32_t row[kMlaIssueMax];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) row[i] = sh.sidx[t0 + gs.row_slot(i)];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) wide_gather_issue(kv, slot_lds(b, i), row[i], gs.col(i));
+  };
+  // Q loads complete before any gather is in flight (a wait for them inside
+  // the tile loop would also wait for the gathers)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  // S^T = K Q^T of the tile in buf for heads h0, h0+16 (2 key blocks x 2
+  // head blocks), optionally issuing this wave's gather slots of another
+  // tile (rows sidx[t0g..], into gbuf) spread over the k-steps
+  auto qk = [&](const uint8_t* tile, f32x4 (&st)[2][2], bool gather, int t0g, int gb) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int koff = (ln & 15) * kPipeRow + (ln >> 4) * 16;
+    auto kfrag = [&](int kb, int ks) {
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(tile + koff + kb * 16 * kPipeRow + ks * 64));
+    };
+    int32_t grow = gather ? sh.sidx[t0g + gs.row_slot(0)] : 0;
+    // K fragments are read kAhead k-steps before their products; the
+    // scheduling barriers keep the compiler from sinking the reads next to
+    // their use (one wave per SIMD: nothing else hides the LDS latency)
+    constexpr int kAhead = 2;
+    bf16x8 kf[kAhead + 1][2];
+#pragma unroll
+    for (int s = 0; s < kAhead; ++s) {
+      kf[s][0] = kfrag(0, s);
+      kf[s][1] = kfrag(1, s);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kMlaKSteps; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + kAhead < kMlaKSteps) {
+        kf[(ks + kAhead) % (kAhead + 1)][0] = kfrag(0, ks + kAhead);
+        kf[(ks + kAhead) % (kAhead + 1)][1] = kfrag(1, ks + kAhead);
+      }
+      const bf16x8 k0 = kf[ks % (kAhead + 1)][0], k1 = kf[ks % (kAhead + 1)][1];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const bf16x8 qv = ks < kQReg ? qf[hb][ks < kQReg ? ks : 0]
+                                     : __builtin_bit_cast(bf16x8, sh.qrope[ks - kQReg][grp][h0 + 16 * hb]);
+        if (ks == 0) {
+          st[0][hb] = mla_qk_first(k0, qv);
+          st[1][hb] = mla_qk_first(k1, qv);
+        } else {
+          mla_qk_acc(st[0][hb], k0, qv);
+          mla_qk_acc(st[1][hb], k1, qv);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (i * kMlaKSteps / kPer == ks && gather) {
+          wide_gather_issue(kv, slot_lds(gb, i), grow, gs.col(i));
+          if (i + 1 < kPer) grow = sh.sidx[t0g + gs.row_slot(i + 1)];
+        }
+      }
+    }
+    mla_qk_settle(st[0][0], st[0][1], st[1][0], st[1][1]);
+  };
+  // scaled logits, masked: st[kb][hb][i] is key 16kb + 4grp + i, head h0+16hb
+  auto logits = [&](f32x4 (&st)[2][2], uint64_t valid, float (&mx)[2]) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb * 16 + grp * 4 + i;
+          const float l = ((valid >> key) & 1ull) ? st[kb][hb][i] * scale2 : -INFINITY;
+          st[kb][hb][i] = l;
+          m = fmaxf(m, l);
+        }
+      mx[hb] = mla_rows_max(m);
+    }
+  };
+
+  float m_ref[2] = {-INFINITY, -INFINITY};
+  bool exact = false;   // m_ref is the exact maximum (after a restart)
+  f32x4 o[kCB][kHG];
+  float l_run[2];
+  for (;;) {
+    if (exact) {
+      // ---- first pass: exact maximum of every head over all rows (tiles
+      //      gathered one at a time into buffer 0)
+      m_ref[0] = m_ref[1] = -INFINITY;
+      for (int32_t t = 0; t < n_tiles; ++t) {
+        __syncthreads();   // buffer 0 free
+        issue_tile(0, t * kPipeTile);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        const int32_t my_row = lane < kPipeTile ? sh.sidx[t * kPipeTile + lane] : -1;
+        const uint64_t valid = __ballot(my_row >= 0);
+        f32x4 st[2][2];
+        qk(g_mla_bufs, st, false, 0, 0);
+        float mx[2];
+        logits(st, valid, mx);
+        m_ref[0] = fmaxf(m_ref[0], mx[0]);
+        m_ref[1] = fmaxf(m_ref[1], mx[1]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int hg = 0; hg < kHG; ++hg) o[cb][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run[0] = l_run[1] = 0.f;
+    if (n_tiles > 0) issue_tile(0, 0);
+    if (n_tiles > 1) issue_tile(1, kPipeTile);
+    bool bailed = false;
+    // tile t lives in buffer t mod 3; its gather was issued two tiles ahead
+    for (int32_t t = 0, b = 0; t < n_tiles; ++t, b = b == 2 ? 0 : b + 1) {
+      if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();       // tile t complete; tile t-1 consumed
+      asm volatile("" ::: "memory");
+      const uint8_t* tile = g_mla_bufs + b * kPipeTileBytes;
+      int lr = lane;
+      asm volatile("" : "+v"(lr));   // recomputed per tile, not kept (and spilled)
+      const int32_t my_row = lr < kPipeTile ? sh.sidx[t * kPipeTile + lr] : -1;
+      const uint64_t valid = __ballot(my_row >= 0);
+      // ---- QK, with the gather of tile t+2 into the buffer of tile t-1
+      f32x4 st[2][2];
+      qk(tile, st, t + 2 < n_tiles, (t + 2) * kPipeTile, b == 0 ? 2 : b - 1);
+      // ---- softmax weights relative to the fixed reference
+      float mx[2];
+      logits(st, valid, mx);
+      bool beyond = false;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        if (t == 0 && !exact) m_ref[hb] = mx[hb];
+        beyond |= mx[hb] > m_ref[hb] + kWideBail;
+        float psum = 0.f;
+        bf16x8 pv;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pw = valid ? __builtin_amdgcn_exp2f(st[kb][hb][i] - m_ref[hb]) : 0.f;
+            psum += pw;
+            pv[kb * 4 + i] = static_cast<__bf16>(pw);
+          }
+        l_run[hb] += mla_rows_sum(psum);
+        sh.p[grp][h0 + 16 * hb] = __builtin_bit_cast(uint4, pv);
+      }
+      if (__ballot(beyond) != 0ull && lane == 0) sh.bail[wave] = 1;
+      // P of every head and the bail flags visible to all waves; only LDS
+      // traffic is waited for (the gathers stay in flight)
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      bool bail = false;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) bail |= sh.bail[w] != 0;
+      if (bail) {
+        bailed = true;
+        break;
+      }
+      // ---- O^T += V^T P^T for this wave's columns, all heads
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int li_t = ln & 15, grp_t = ln >> 4;
+      const int voff = (4 * grp_t + (li_t >> 2)) * kPipeRow + ((li_t & 3) >> 1) * 16 +
+                       (li_t & 1) * 8 + wave * kCols * 2;
+#pragma unroll
+      for (int c0 = 0; c0 < kCB; c0 += kCBC) {
+        bf16x8 vf[kCBC];
+#pragma unroll
+        for (int c = 0; c < kCBC; ++c) {
+          const int cb = c0 + c;
+          if constexpr (kTrV) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(tile + voff + cb * 32));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(tile + voff + 16 * kPipeRow + cb * 32));
+            vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          } else {
+            const int col = wave * kCols + cb * 16 + li;
+            const uint8_t* p0 = tile + 4 * grp * kPipeRow + (col >> 3) * 16 + (col & 7) * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              vf[c][i] = *reinterpret_cast<const __bf16*>(p0 + i * kPipeRow);
+              vf[c][4 + i] = *reinterpret_cast<const __bf16*>(p0 + (16 + i) * kPipeRow);
+            }
+          }
+        }
+        bf16x8 pf = __builtin_bit_cast(bf16x8, sh.p[grp_t][li_t]);
+#pragma unroll
+        for (int hg = 0; hg < kHG; ++hg) {
+          bf16x8 pn = pf;
+          if (hg + 1 < kHG) pn = __builtin_bit_cast(bf16x8, sh.p[grp_t][(hg + 1) * 16 + li_t]);
+#pragma unroll
+          for (int c = 0; c < kCBC; ++c)
+            o[c0 + c][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c], pf, o[c0 + c][hg], 0, 0, 0);
+          pf = pn;
+        }
+      }
+    }
+    if (!bailed) break;
+    // start over with the exact maximum: drain the gathers in flight first
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (tid < kNW) sh.bail[tid] = 0;
+    exact = true;
+  }
+
+  // ---- epilogue: owners publish (m, l); every wave writes its columns
+  if (lane < 16) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      sh.m_fin[h0 + 16 * hb] = m_ref[hb];
+      sh.l_fin[h0 + 16 * hb] = l_run[hb];
+    }
+  }
+  __syncthreads();
+  const int col0 = wave * kCols + grp * 4;
+#pragma unroll
+  for (int hg = 0; hg < kHG; ++hg) {
+    const int h = hg * 16 + li;
+    const float lf = sh.l_fin[h];
+    if (a.n_splits == 1) {
+      const float inv = lf > 0.f ? 1.f / lf : 0.f;
+      const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + col0;
+      if (a.out_dtype == DS_BF16) {
+        uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) {
+          uint2 pk;
+          pk.x = f32_to_bf16_bits(o[cb][hg][0] * inv) |
+                 (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][1] * inv)) << 16);
+          pk.y = f32_to_bf16_bits(o[cb][hg][2] * inv) |
+                 (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(out + cb * 16) = pk;
+        }
+      } else {
+        float* out = static_cast<float*>(a.out) + obase;
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+          *reinterpret_cast<float4*>(out + cb * 16) =
+              make_float4(o[cb][hg][0] * inv, o[cb][hg][1] * inv, o[cb][hg][2] * inv,
+                          o[cb][hg][3] * inv);
+      }
+    } else {
+      float* po = static_cast<float*>(a.ws) +
+                  ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * kMlaDl + col0;
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+        *reinterpret_cast<float4*>(po + cb * 16) =
+            make_float4(o[cb][hg][0], o[cb][hg][1], o[cb][hg][2], o[cb][hg][3]);
+    }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = h0 + 16 * hb;
+      if (a.n_splits == 1) {
+        if (a.lse)
+          a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
+              l_run[hb] > 0.f ? (m_ref[hb] + log2f(l_run[hb])) * kLn2 : -INFINITY;
+      } else {
+        float* pml = static_cast<float*>(a.ws) +
+                     static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl +
+                     ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * 2;
+        pml[0] = m_ref[hb];
+        pml[1] = l_run[hb];
+      }
+    }
+  }
+}
+
 // Merge split partials: one workgroup per (query, head), one thread per
 // output column pair.
 __global__ void __launch_bounds__(256)
@@ -935,8 +1384,10 @@ ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
       static_cast<int32_t>(round_up(ceil_div(a.topk, a.n_splits), kMlaTile));
   const int64_t blocks = static_cast<int64_t>(a.n_q) * a.n_splits;
   const bool tr = mla_transpose_reads();
+  // the wide kernel addresses rows with 32-bit offsets
+  const bool wide = static_cast<uint64_t>(a.kv_rows) * kMlaRowBytes < (1ull << 32);
   if (a.kv_dtype == DS_BF16) {
-    switch (a.n_heads) {
+    if (!wide) switch (a.n_heads) {
       case 32:
         if (tr) mla_bf16_pipelined_kernel<true, 1><<<blocks, kWave * 2, 0, s>>>(a, per_split);
         else mla_bf16_pipelined_kernel<false, 1><<<blocks, kWave * 2, 0, s>>>(a, per_split);
@@ -948,6 +1399,19 @@ ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
       default:
         if (tr) mla_bf16_pipelined_kernel<true, 4><<<blocks, kWave * 8, 0, s>>>(a, per_split);
         else mla_bf16_pipelined_kernel<false, 4><<<blocks, kWave * 8, 0, s>>>(a, per_split);
+    }
+    else switch (a.n_heads) {
+      case 32:
+        if (tr) mla_bf16_wide_kernel<true, 1><<<blocks, kWave * 1, 0, s>>>(a, per_split);
+        else mla_bf16_wide_kernel<false, 1><<<blocks, kWave * 1, 0, s>>>(a, per_split);
+        break;
+      case 64:
+        if (tr) mla_bf16_wide_kernel<true, 2><<<blocks, kWave * 2, 0, s>>>(a, per_split);
+        else mla_bf16_wide_kernel<false, 2><<<blocks, kWave * 2, 0, s>>>(a, per_split);
+        break;
+      default:
+        if (tr) mla_bf16_wide_kernel<true, 4><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+        else mla_bf16_wide_kernel<false, 4><<<blocks, kWave * 4, 0, s>>>(a, per_split);
     }
     ds_status st = check_launch("sparse_mla");
     if (st != DS_OK || a.n_splits == 1) return st;
