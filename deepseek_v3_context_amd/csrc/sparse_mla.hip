@@ -1055,6 +1055,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
           bf16x8, *reinterpret_cast<const uint4*>(tile + koff + kb * 16 * kPipeRow + ks * 64));
     };
     int32_t grow = gather ? sh.sidx[t0g + gs.row_slot(0)] : 0;
+    f32x4 su[2][2];
     // K fragments are read kAhead k-steps before their products; the
     // scheduling barriers keep the compiler from sinking the reads next to
     // their use (one wave per SIMD: nothing else hides the LDS latency)
@@ -1077,12 +1078,14 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       for (int hb = 0; hb < 2; ++hb) {
         const bf16x8 qv = ks < kQReg ? qf[hb][ks < kQReg ? ks : 0]
                                      : __builtin_bit_cast(bf16x8, sh.qrope[ks - kQReg][grp][h0 + 16 * hb]);
-        if (ks == 0) {
-          st[0][hb] = mla_qk_first(k0, qv);
-          st[1][hb] = mla_qk_first(k1, qv);
+        // even and odd k-steps accumulate separately: 8 independent chains
+        f32x4 (&acc)[2][2] = (ks & 1) ? su : st;
+        if (ks < 2) {
+          acc[0][hb] = mla_qk_first(k0, qv);
+          acc[1][hb] = mla_qk_first(k1, qv);
         } else {
-          mla_qk_acc(st[0][hb], k0, qv);
-          mla_qk_acc(st[1][hb], k1, qv);
+          mla_qk_acc(acc[0][hb], k0, qv);
+          mla_qk_acc(acc[1][hb], k1, qv);
         }
       }
 #pragma unroll
@@ -1094,6 +1097,11 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       }
     }
     mla_qk_settle(st[0][0], st[0][1], st[1][0], st[1][1]);
+    mla_qk_settle(su[0][0], su[0][1], su[1][0], su[1][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) st[kb][hb] += su[kb][hb];
   };
   // scaled logits, masked: st[kb][hb][i] is key 16kb + 4grp + i, head h0+16hb
   auto logits = [&](f32x4 (&st)[2][2], uint64_t valid, float (&mx)[2]) {
