@@ -968,8 +968,12 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   // accumulators (O^T) in the accumulator file.
   asm volatile("" ::: "a0");
 
-  const int32_t j = blockIdx.x / a.n_splits;
-  const int32_t split = blockIdx.x - j * a.n_splits;
+  // Queries in reverse order: in causal prefill the later queries select
+  // the most rows, so the longest workgroups start first and the short ones
+  // fill the tail.
+  const int32_t jr = blockIdx.x / a.n_splits;
+  const int32_t split = blockIdx.x - jr * a.n_splits;
+  const int32_t j = a.n_q - 1 - jr;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
