@@ -200,10 +200,15 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
   // the tile loop would make every wait for the next tile's gather
   // (vmcnt counts stores too) also wait for the store to retire
   __shared__ float sc[kIxPWaves][chunk_keys];
-  const uint32_t id = xcd_contiguous_id(blockIdx.x, grid);
+  // Every workgroup reads the same key rows (the whole indexer key set of
+  // a prefill fits in each XCD's L2), so workgroups are left in the
+  // hardware's round-robin order over the XCDs, which spreads the causal
+  // work evenly; query blocks run in reverse so the longest rows start
+  // first.
+  const uint32_t id = blockIdx.x;
   if (id >= static_cast<uint32_t>(n_qblocks) * n_chunks) return;
-  const int32_t qb = id / n_chunks;
-  const int32_t chunk = id - qb * n_chunks;
+  const int32_t qb = n_qblocks - 1 - static_cast<int32_t>(id / n_chunks);
+  const int32_t chunk = static_cast<int32_t>(id % n_chunks);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

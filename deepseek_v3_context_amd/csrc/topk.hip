@@ -9,18 +9,18 @@
 //
 // One workgroup per query row.  Scores are mapped to order-preserving
 // 32-bit keys and the k-th largest key is found by four 8-bit radix passes
-// (LDS histogram + one-wave suffix scan per pass).  Rows that fit are
-// cached in LDS so the passes never return to HBM; longer rows stream from
-// L2/HBM.  A final ordered pass (ballot + per-wave counts) writes the
-// selected positions in ascending order: every key above the threshold and
-// the lowest-position keys equal to it, so the selected set is exactly the
-// tie-to-lower-position set and the output is deterministic.
+// (per-wave LDS histograms + one-wave suffix scan per pass).  Rows that fit
+// are cached in LDS so the passes never return to memory; longer rows are
+// staged through LDS block by block on every pass.  A final ordered pass
+// (block-wide scans) writes the selected positions in ascending order:
+// every key above the threshold and the lowest-position keys equal to it,
+// so the selected set is exactly the tie-to-lower-position set and the
+// output is deterministic.
 #include "common.h"
 
 namespace ds32cp {
 
-constexpr int kTkThreads = 512;
-constexpr int kTkWaves = kTkThreads / kWave;
+constexpr int kTkPer = 8;                 // consecutive keys per thread and step
 constexpr int32_t kTkCacheKeys = 32768;   // 128 KiB of LDS
 
 __device__ __forceinline__ int64_t topk_key_row(const TopkArgs& a, int32_t req,
@@ -35,12 +35,40 @@ __device__ __forceinline__ int64_t topk_key_row(const TopkArgs& a, int32_t req,
   return (pid >= 0 && row < a.k_rows) ? row : -1;
 }
 
+// Exclusive prefix sum of one count per thread over the workgroup, in
+// thread order, plus the total.  Uses wave_tot (one slot per wave); two
+// barriers.
+template <int kTkWaves>
+__device__ __forceinline__ uint32_t tk_block_scan(uint32_t v, int lane, int wave,
+                                                  uint32_t* wave_tot, uint32_t& total) {
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const uint32_t c = wave_tot[w];
+    before += w < wave ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();   // wave_tot may be reused right after
+  total = tot;
+  return before + incl - v;
+}
+
+template <int kTkThreads>
 __global__ void __launch_bounds__(kTkThreads)
 topk_kernel(TopkArgs a, int32_t cache_keys) {
-  extern __shared__ uint32_t cache[];
-  __shared__ uint32_t hist[256];
+  constexpr int kTkWaves = kTkThreads / kWave;
+  extern __shared__ __align__(16) uint32_t cache[];
+  __shared__ uint32_t hist[kTkWaves][256];   // one histogram per wave (less contention)
   __shared__ uint32_t sh_digit, sh_remaining;
-  __shared__ uint32_t wave_eq[kTkWaves];
+  __shared__ uint32_t wave_tot[kTkWaves];
 
   const int32_t j = blockIdx.x;
   const int tid = threadIdx.x;
@@ -63,28 +91,86 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
     return;
   }
 
+  // The row is processed in blocks of cache_keys keys staged in LDS as
+  // order-preserving keys (one block, loaded once, when the row fits).  A
+  // block load keeps many loads in flight per thread, and every pass over
+  // a block handles kTkPer consecutive keys per thread per step, so that
+  // neither memory nor LDS latency is paid per key.
   const bool cached = L <= cache_keys;
-  if (cached) {
-    for (int32_t t = tid; t < L; t += kTkThreads) cache[t] = float_order_key(row_scores[t]);
-  }
-  auto key_at = [&](int32_t t) -> uint32_t {
-    return cached ? cache[t] : float_order_key(row_scores[t]);
+  auto block_len = [&](int32_t b0) { return L - b0 < cache_keys ? L - b0 : cache_keys; };
+  auto load_block = [&](int32_t b0) {
+    const int32_t n = block_len(b0);
+    constexpr int kU = 16;
+    for (int32_t r0 = 0; r0 < n; r0 += kU * kTkThreads) {
+      float v[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int32_t t = r0 + k * kTkThreads + tid;
+        v[k] = t < n ? row_scores[b0 + t] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int32_t t = r0 + k * kTkThreads + tid;
+        if (t < n) cache[t] = float_order_key(v[k]);
+      }
+    }
+    __syncthreads();
   };
+  // keys t0 .. t0+kTkPer-1 of the staged block (past its end: 0, and
+  // masked out by the callers)
+  auto read_keys = [&](int32_t t0, int32_t n, uint32_t (&u)[kTkPer]) {
+    if (t0 + kTkPer <= n) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&cache[t0]);
+      const uint4 y = *reinterpret_cast<const uint4*>(&cache[t0 + 4]);
+      u[0] = x.x; u[1] = x.y; u[2] = x.z; u[3] = x.w;
+      u[4] = y.x; u[5] = y.y; u[6] = y.z; u[7] = y.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < kTkPer; ++k) u[k] = t0 + k < n ? cache[t0 + k] : 0u;
+    }
+  };
+  if (cached) load_block(0);
 
   uint32_t prefix = 0, mask = 0, remaining = static_cast<uint32_t>(a.topk);
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kTkThreads) hist[i] = 0;
+    for (int i = tid; i < kTkWaves * 256; i += kTkThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int32_t t = tid; t < L; t += kTkThreads) {
-      const uint32_t u = key_at(t);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    for (int32_t b0 = 0; b0 < L; b0 += cache_keys) {
+      if (!cached) {
+        __syncthreads();   // the previous block is fully counted
+        load_block(b0);
+      }
+      const int32_t n = block_len(b0);
+      for (int32_t t0 = tid * kTkPer; t0 < n; t0 += kTkThreads * kTkPer) {
+        uint32_t u[kTkPer];
+        read_keys(t0, n, u);
+#pragma unroll
+        for (int k = 0; k < kTkPer; ++k) {
+          const bool in = t0 + k < n && (u[k] & mask) == prefix;
+          const uint32_t d = (u[k] >> shift) & 255u;
+          // Scores of a row often share their top bits: lanes of the wave
+          // with the digit of the first active lane are counted with one add.
+          const uint64_t act = __ballot(in);
+          if (act == 0ull) continue;
+          const int first = static_cast<int>(__builtin_ctzll(act));
+          const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
+          const uint64_t same = __ballot(in && d == d0);
+          if (lane == first) atomicAdd(&hist[wave][d0], static_cast<uint32_t>(__popcll(same)));
+          if (in && d != d0) atomicAdd(&hist[wave][d], 1u);
+        }
+      }
     }
     __syncthreads();
     if (wave == 0) {
       // lane l owns digits 4l..4l+3; scan counts from the largest digit down
       uint32_t c[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) c[b] = hist[4 * lane + b];
+      for (int b = 0; b < 4; ++b) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int w = 0; w < kTkWaves; ++w) v += hist[w][4 * lane + b];
+        c[b] = v;
+      }
       const uint32_t mine = c[0] + c[1] + c[2] + c[3];
       uint32_t incl = mine;  // sum over lanes >= this lane
 #pragma unroll
@@ -112,49 +198,54 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   // prefix is now the k-th largest key; `remaining` copies of it are taken.
   // One ordered pass writes every selected position in ascending order:
   // keys above the threshold, and the first `remaining` keys equal to it.
+  // Thread t covers kTkPer consecutive positions of each step; two block
+  // scans (equal keys, then taken keys) give every key its rank.
   uint32_t taken = 0, eq_seen = 0;
-  for (int32_t base = 0; base < L; base += kTkThreads) {
-    const int32_t t = base + tid;
-    const uint32_t u = t < L ? key_at(t) : 0u;
-    const bool gt = t < L && u > prefix;
-    const bool eq = t < L && u == prefix;
-    const uint64_t ball_eq = __ballot(eq);
-    // an equal key is taken when fewer than `remaining` equal keys precede it
-    const uint32_t eq_rank_in_wave = static_cast<uint32_t>(__popcll(ball_eq & ((1ull << lane) - 1ull)));
-    if (lane == 0) wave_eq[wave] = static_cast<uint32_t>(__popcll(ball_eq));
-    __syncthreads();
-    uint32_t eq_before = eq_seen;
-    uint32_t eq_total = 0;
-#pragma unroll
-    for (int w = 0; w < kTkWaves; ++w) {
-      const uint32_t cnt = wave_eq[w];
-      eq_before += w < wave ? cnt : 0u;
-      eq_total += cnt;
+  for (int32_t b0 = 0; b0 < L && taken < static_cast<uint32_t>(a.topk); b0 += cache_keys) {
+    if (!cached) {
+      __syncthreads();
+      load_block(b0);
     }
-    const bool take = gt || (eq && eq_before + eq_rank_in_wave < remaining);
-    const uint64_t ball_take = __ballot(take);
-    __syncthreads();   // wave_eq is reused below
-    if (lane == 0) wave_eq[wave] = static_cast<uint32_t>(__popcll(ball_take));
-    __syncthreads();
-    uint32_t take_before = taken, take_total = 0;
+    const int32_t n = block_len(b0);
+    for (int32_t s0 = 0; s0 < n; s0 += kTkThreads * kTkPer) {
+      const int32_t t0 = s0 + tid * kTkPer;
+      uint32_t u[kTkPer];
+      read_keys(t0, n, u);
+      uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int w = 0; w < kTkWaves; ++w) {
-      const uint32_t cnt = wave_eq[w];
-      take_before += w < wave ? cnt : 0u;
-      take_total += cnt;
-    }
-    if (take) {
-      const uint32_t slot = take_before +
-          static_cast<uint32_t>(__popcll(ball_take & ((1ull << lane) - 1ull)));
-      if (slot < static_cast<uint32_t>(a.topk)) {
-        out_idx[slot] = static_cast<int32_t>(topk_key_row(a, req, kv0 + t));
-        if (out_score) out_score[slot] = order_key_to_float(u);
+      for (int k = 0; k < kTkPer; ++k) {
+        const bool v = t0 + k < n;
+        gt |= (v && u[k] > prefix) ? 1u << k : 0u;
+        eq |= (v && u[k] == prefix) ? 1u << k : 0u;
       }
+      uint32_t eq_total;
+      const uint32_t eq_before = eq_seen + tk_block_scan<kTkWaves>(__popc(eq), lane, wave, wave_tot, eq_total);
+      // equal keys are taken while fewer than `remaining` precede them
+      uint32_t take = gt;
+      uint32_t r = eq_before;
+#pragma unroll
+      for (int k = 0; k < kTkPer; ++k) {
+        if ((eq >> k) & 1u) {
+          if (r < remaining) take |= 1u << k;
+          ++r;
+        }
+      }
+      uint32_t take_total;
+      uint32_t slot = taken + tk_block_scan<kTkWaves>(__popc(take), lane, wave, wave_tot, take_total);
+#pragma unroll
+      for (int k = 0; k < kTkPer; ++k) {
+        if ((take >> k) & 1u) {
+          if (slot < static_cast<uint32_t>(a.topk)) {
+            out_idx[slot] = static_cast<int32_t>(topk_key_row(a, req, kv0 + b0 + t0 + k));
+            if (out_score) out_score[slot] = order_key_to_float(u[k]);
+          }
+          ++slot;
+        }
+      }
+      taken += take_total;
+      eq_seen += eq_total;
+      if (taken >= static_cast<uint32_t>(a.topk)) break;   // uniform: all threads agree
     }
-    taken += take_total;
-    eq_seen += eq_total;
-    __syncthreads();
-    if (taken >= static_cast<uint32_t>(a.topk)) break;   // uniform: all threads agree
   }
 }
 
@@ -164,12 +255,17 @@ ds_status launch_topk(const TopkArgs& a, hipStream_t s) {
   const size_t smem = sizeof(uint32_t) * static_cast<size_t>(cache_keys > 0 ? cache_keys : 1);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(sizeof(uint32_t) * kTkCacheKeys));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<512>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(sizeof(uint32_t) * kTkCacheKeys));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<1024>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(sizeof(uint32_t) * kTkCacheKeys));
     attr_set = true;
   }
-  topk_kernel<<<a.n_q, kTkThreads, smem, s>>>(a, cache_keys);
+  // long rows: more waves per row to keep more keys in flight
+  if (a.max_kv_len > 16384) topk_kernel<1024><<<a.n_q, 1024, smem, s>>>(a, cache_keys);
+  else topk_kernel<512><<<a.n_q, 512, smem, s>>>(a, cache_keys);
   return check_launch("topk_select");
 }
 
