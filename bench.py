@@ -7,7 +7,8 @@ already resident in HBM:
   prefill: cp_split_metadata (+ row gather of the input token ids),
            kv_rerange of the latent KV and of the indexer keys,
            indexer scores + top-k, sparse MLA (prefill kernel);
-  decode:  indexer scores + top-k on the paged pool, sparse MLA (decode).
+  decode:  indexer_topk (scores + top-k in one call) on the paged pool,
+           sparse MLA (decode).
 
 The step is timed end to end (K steps between two device synchronisations)
 and per call with HIP events on the stream the library launches on.  The
@@ -152,7 +153,7 @@ def setup_decode(wl, torch, ds, dev):
           "q": up(inp["q"], wl.act_fmt), "max_len": max_len,
           "kv_scale": None if inp["kv_scale"] is None else torch.from_numpy(inp["kv_scale"]).to(dev),
           "ki_scale": None if inp["k_idx_scale"] is None else torch.from_numpy(inp["k_idx_scale"]).to(dev)}
-    st["scores"] = torch.empty((n, ((max_len + 63) // 64) * 64), dtype=torch.float32, device=dev)
+    st["ix_ws"] = torch.empty(ds.indexer_topk_workspace_size(n, max_len), dtype=torch.uint8, device=dev)
     st["topk_idx"] = torch.empty((n, wl.topk), dtype=torch.int32, device=dev)
     st["out"] = torch.empty((n, wl.n_heads, wl.d_latent), dtype=torch.bfloat16, device=dev)
     st["lse"] = torch.empty((n, wl.n_heads), dtype=torch.float32, device=dev)
@@ -164,9 +165,7 @@ def setup_decode(wl, torch, ds, dev):
 def decode_step(wl, ds, st, tm):
     m = st["meta"]
     paging = dict(q_req=m["q_req"], page_table=st["table"], page_size=wl.page_size)
-    k_rows = st["ki"].shape[0]
-    tm.run("indexer_scores", lambda: ds.indexer_scores(st["q_idx"], st["w"], st["ki"], m["kv_start"], m["kv_len"], st["max_len"], k_scale=st["ki_scale"], scores=st["scores"], **paging))
-    tm.run("topk_select", lambda: ds.topk_select(st["scores"], m["kv_start"], m["kv_len"], st["max_len"], wl.topk, k_rows, topk_idx=st["topk_idx"], **paging))
+    tm.run("indexer_topk", lambda: ds.indexer_topk(st["q_idx"], st["w"], st["ki"], m["kv_start"], m["kv_len"], st["max_len"], wl.topk, k_scale=st["ki_scale"], topk_idx=st["topk_idx"], workspace=st["ix_ws"], **paging))
     tm.run("sparse_mla", lambda: ds.sparse_mla_decode(st["q"], st["kv"], st["topk_idx"], wl.scale, wl.d_latent, kv_scale=st["kv_scale"], out=st["out"], lse=st["lse"], workspace=st["ws"]))
 
 
@@ -174,7 +173,8 @@ def decode_step(wl, ds, st, tm):
 # while these files are unchanged since the counters were taken)
 CALL_SOURCES = {"sparse_mla": ("sparse_mla.hip", "common.h"),
                 "indexer_scores": ("indexer.hip", "common.h"),
-                "topk_select": ("topk.hip", "common.h")}
+                "topk_select": ("topk.hip", "common.h"),
+                "indexer_topk": ("indexer.hip", "topk.hip", "common.h")}
 
 
 def counted_traffic(call, workload):
@@ -224,6 +224,11 @@ def work_model(wl, kv_len):
                            "bytes": n * wl.h_idx * (wl.d_idx * act + 4)
                            + (T if T else idx_pairs) * wl.d_idx * kvb + idx_pairs * 4},
         "topk_select": {"flops": 0, "bytes": idx_pairs * 4 + n * wl.topk * 4},
+        # indexer + top-k in one call (decode): keys and queries read once, the
+        # scores written and read back once, the selection written
+        "indexer_topk": {"flops": idx_flops,
+                         "bytes": n * wl.h_idx * (wl.d_idx * act + 4) + idx_pairs * wl.d_idx * kvb
+                         + 2 * idx_pairs * 4 + n * wl.topk * 4},
         "sparse_mla": {"flops": mla_flops,
                        "bytes": n * wl.n_heads * (wl.d_qk * act + wl.d_latent * 2 + 4)
                        + mla_pairs * wl.d_qk * kvb + n * wl.topk * 4},

@@ -126,7 +126,9 @@ static ds_status check_indexer(const char* fn, const IndexerArgs& a) {
 
 size_t indexer_topk_workspace_size(int32_t n_q, int32_t max_kv_len) {
   if (n_q <= 0 || max_kv_len <= 0) return 256;
-  return sizeof(float) * static_cast<size_t>(n_q) * static_cast<size_t>(round_up(max_kv_len, 64));
+  size_t bytes = sizeof(float) * static_cast<size_t>(n_q) * static_cast<size_t>(round_up(max_kv_len, 64));
+  if (topk_two_phase(n_q, max_kv_len)) bytes += topk_two_phase_bytes(n_q, max_kv_len);
+  return bytes;
 }
 
 ds_status indexer_scores(const void* q_idx, ds_dtype q_dtype, const float* w,
@@ -202,6 +204,15 @@ ds_status indexer_topk(const void* q_idx, ds_dtype q_dtype, const float* w,
   if (st != DS_OK) return st;
   TopkArgs t{static_cast<const float*>(ws), stride, kv_start, kv_len, q_req, page_table,
              n_req, page_size, max_pages, k_rows, n_q, max_kv_len, topk, topk_idx, topk_score};
+  if (topk_two_phase(n_q, max_kv_len)) {
+    // few long rows: per-segment candidates after the scores
+    t.n_seg = static_cast<int32_t>(ceil_div(max_kv_len, kTopkSegLen));
+    t.seg_len = kTopkSegLen;
+    uint8_t* base = static_cast<uint8_t*>(ws) + sizeof(float) * static_cast<size_t>(n_q) * stride;
+    t.cand_score = reinterpret_cast<float*>(base);
+    t.cand_pos = reinterpret_cast<int32_t*>(base + sizeof(float) * static_cast<size_t>(n_q) *
+                                                     t.n_seg * kTopkMax);
+  }
   return launch_topk(t, stream);
 }
 

@@ -129,8 +129,24 @@ struct TopkArgs {
   int32_t n_q, max_kv_len, topk;
   int32_t* topk_idx;
   float* topk_score;
+  // two-phase selection of long rows (see topk.hip): per-segment
+  // candidates, n_seg segments of seg_len positions per row, topk each
+  float* cand_score = nullptr;
+  int32_t* cand_pos = nullptr;
+  int32_t n_seg = 0, seg_len = 0;
 };
 ds_status launch_topk(const TopkArgs& a, hipStream_t s);
+// Rows longer than this are selected in two phases when there are few of
+// them (their candidates need topk_two_phase_bytes() of workspace).
+constexpr int32_t kTopkSegLen = 8192;
+constexpr int32_t kTopkMax = 2048;
+inline bool topk_two_phase(int32_t n_q, int32_t max_kv_len) {
+  return max_kv_len > 2 * kTopkSegLen && n_q <= 256;
+}
+inline size_t topk_two_phase_bytes(int32_t n_q, int32_t max_kv_len) {
+  const int64_t n_seg = (static_cast<int64_t>(max_kv_len) + kTopkSegLen - 1) / kTopkSegLen;
+  return static_cast<size_t>(n_q) * n_seg * kTopkMax * (sizeof(float) + sizeof(int32_t));
+}
 
 struct MlaArgs {
   const void* q;

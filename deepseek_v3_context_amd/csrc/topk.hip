@@ -61,7 +61,17 @@ __device__ __forceinline__ uint32_t tk_block_scan(uint32_t v, int lane, int wave
   return before + incl - v;
 }
 
-template <int kTkThreads>
+// kMode 0: one workgroup selects a whole row.
+// kMode 1 (two-phase, first phase): workgroup (row, s) selects the top-k of
+//   positions [s*seg_len, (s+1)*seg_len) of its row and writes them, in
+//   position order and padded to k entries (score -inf, position -1), to
+//   the row's candidate list.  The row's top-k is a subset of the union of
+//   its segments' top-k (ties included: a segment keeps its lowest
+//   positions among equal scores), so nothing is lost.
+// kMode 2 (second phase): one workgroup selects the row's top-k from its
+//   n_seg*k candidates, which are in position order; padding scores are
+//   -inf, below every real (finite) indexer score.
+template <int kTkThreads, int kMode>
 __global__ void __launch_bounds__(kTkThreads)
 topk_kernel(TopkArgs a, int32_t cache_keys) {
   constexpr int kTkWaves = kTkThreads / kWave;
@@ -70,7 +80,8 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   __shared__ uint32_t sh_digit, sh_remaining;
   __shared__ uint32_t wave_tot[kTkWaves];
 
-  const int32_t j = blockIdx.x;
+  const int32_t j = kMode == 1 ? static_cast<int32_t>(blockIdx.x / a.n_seg) : blockIdx.x;
+  const int32_t seg = kMode == 1 ? static_cast<int32_t>(blockIdx.x % a.n_seg) : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -81,12 +92,47 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   float* out_score = a.topk_score ? a.topk_score + static_cast<int64_t>(j) * a.topk : nullptr;
   const int32_t req = a.q_req ? a.q_req[j] : 0;
   const int64_t kv0 = a.kv_start[j];
+  const int64_t cbase = static_cast<int64_t>(j) * a.n_seg * a.topk;   // row's candidates
+  int32_t pos0 = 0;   // logical position of element 0 (kMode 1)
+  if constexpr (kMode == 1) {
+    pos0 = seg * a.seg_len;
+    L = L - pos0 < a.seg_len ? L - pos0 : a.seg_len;
+    L = L < 0 ? 0 : L;
+    row_scores += pos0;
+  } else if constexpr (kMode == 2) {
+    row_scores = a.cand_score + cbase;
+    if (L > a.topk) L = a.n_seg * a.topk;
+  }
+  // logical position (within the row) of element t, -1 for padding
+  auto pos_of = [&](int32_t t) -> int64_t {
+    if constexpr (kMode == 2) return a.cand_pos[cbase + t];
+    return pos0 + t;
+  };
+  // the slot-th selected element (position order) is element t
+  auto emit = [&](uint32_t slot, int32_t t, float score) {
+    if constexpr (kMode == 1) {
+      const int64_t c = cbase + static_cast<int64_t>(seg) * a.topk + slot;
+      a.cand_score[c] = score;
+      a.cand_pos[c] = static_cast<int32_t>(pos_of(t));
+    } else {
+      const int64_t p = pos_of(t);
+      out_idx[slot] = p >= 0 ? static_cast<int32_t>(topk_key_row(a, req, kv0 + p)) : -1;
+      if (out_score) out_score[slot] = score;
+    }
+  };
 
-  if (L <= a.topk) {  // every causal key is selected
+  if (L <= a.topk) {  // every key is selected
     for (int32_t t = tid; t < a.topk; t += kTkThreads) {
-      const bool take = t < L;
-      out_idx[t] = take ? static_cast<int32_t>(topk_key_row(a, req, kv0 + t)) : -1;
-      if (out_score) out_score[t] = take ? row_scores[t] : -INFINITY;
+      if (t < L) {
+        emit(t, t, row_scores[t]);
+      } else if constexpr (kMode == 1) {
+        const int64_t c = cbase + static_cast<int64_t>(seg) * a.topk + t;
+        a.cand_score[c] = -INFINITY;
+        a.cand_pos[c] = -1;
+      } else {
+        out_idx[t] = -1;
+        if (out_score) out_score[t] = -INFINITY;
+      }
     }
     return;
   }
@@ -235,10 +281,7 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
 #pragma unroll
       for (int k = 0; k < kTkPer; ++k) {
         if ((take >> k) & 1u) {
-          if (slot < static_cast<uint32_t>(a.topk)) {
-            out_idx[slot] = static_cast<int32_t>(topk_key_row(a, req, kv0 + b0 + t0 + k));
-            if (out_score) out_score[slot] = order_key_to_float(u[k]);
-          }
+          if (slot < static_cast<uint32_t>(a.topk)) emit(slot, b0 + t0 + k, order_key_to_float(u[k]));
           ++slot;
         }
       }
@@ -249,23 +292,40 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   }
 }
 
+template <int kThreads, int kMode>
+static void topk_set_smem() {
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<kThreads, kMode>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(sizeof(uint32_t) * kTkCacheKeys));
+}
+
 ds_status launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.n_q == 0) return DS_OK;
-  const int32_t cache_keys = a.max_kv_len < kTkCacheKeys ? a.max_kv_len : kTkCacheKeys;
-  const size_t smem = sizeof(uint32_t) * static_cast<size_t>(cache_keys > 0 ? cache_keys : 1);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<512>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(sizeof(uint32_t) * kTkCacheKeys));
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<1024>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(sizeof(uint32_t) * kTkCacheKeys));
+    topk_set_smem<512, 0>();
+    topk_set_smem<1024, 0>();
+    topk_set_smem<512, 1>();
+    topk_set_smem<1024, 2>();
     attr_set = true;
   }
+  if (a.cand_score != nullptr) {
+    // two phases: segments of kTopkSegLen positions (cached in LDS), then
+    // the candidates of each row (n_seg * topk, cached in LDS)
+    const size_t smem1 = sizeof(uint32_t) * kTopkSegLen;
+    topk_kernel<512, 1><<<a.n_q * a.n_seg, 512, smem1, s>>>(a, kTopkSegLen);
+    ds_status st = check_launch("topk_select (segments)");
+    if (st != DS_OK) return st;
+    const int32_t nc = a.n_seg * a.topk;
+    const int32_t cache2 = nc < kTkCacheKeys ? nc : kTkCacheKeys;
+    topk_kernel<1024, 2><<<a.n_q, 1024, sizeof(uint32_t) * cache2, s>>>(a, cache2);
+    return check_launch("topk_select (candidates)");
+  }
+  const int32_t cache_keys = a.max_kv_len < kTkCacheKeys ? a.max_kv_len : kTkCacheKeys;
+  const size_t smem = sizeof(uint32_t) * static_cast<size_t>(cache_keys > 0 ? cache_keys : 1);
   // long rows: more waves per row to keep more keys in flight
-  if (a.max_kv_len > 16384) topk_kernel<1024><<<a.n_q, 1024, smem, s>>>(a, cache_keys);
-  else topk_kernel<512><<<a.n_q, 512, smem, s>>>(a, cache_keys);
+  if (a.max_kv_len > 16384) topk_kernel<1024, 0><<<a.n_q, 1024, smem, s>>>(a, cache_keys);
+  else topk_kernel<512, 0><<<a.n_q, 512, smem, s>>>(a, cache_keys);
   return check_launch("topk_select");
 }
 
