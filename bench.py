@@ -116,6 +116,8 @@ def setup_prefill(wl, torch, ds, dev):
     st["topk_idx"] = torch.empty((n, wl.topk), **i32)
     st["out"] = torch.empty((n, wl.n_heads, wl.d_latent), dtype=torch.bfloat16 if wl.act_fmt != "f32" else torch.float32, device=dev)
     st["lse"] = torch.empty((n, wl.n_heads), dtype=torch.float32, device=dev)
+    need = ds.sparse_mla_prefill_workspace_size(st["kv"].shape[0], st["kv"].dtype)
+    st["mla_ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     return st
 
 
@@ -127,7 +129,7 @@ def prefill_step(wl, ds, st, tm):
     tm.run("kv_rerange(indexer_k)", lambda: ds.kv_rerange(st["ki_cat"], st["slot"], T, cp, out=st["ki"]))
     tm.run("indexer_scores", lambda: ds.indexer_scores(st["q_idx"], st["w"], st["ki"], m["kv_start"], m["kv_len"], st["max_len"], k_scale=st["ki_scale"], scores=st["scores"]))
     tm.run("topk_select", lambda: ds.topk_select(st["scores"], m["kv_start"], m["kv_len"], st["max_len"], wl.topk, T, topk_idx=st["topk_idx"]))
-    tm.run("sparse_mla", lambda: ds.sparse_mla_prefill(st["q"], st["kv"], st["topk_idx"], wl.scale, wl.d_latent, kv_scale=st["kv_scale"], out=st["out"], lse=st["lse"]))
+    tm.run("sparse_mla", lambda: ds.sparse_mla_prefill(st["q"], st["kv"], st["topk_idx"], wl.scale, wl.d_latent, kv_scale=st["kv_scale"], out=st["out"], lse=st["lse"], workspace=st["mla_ws"]))
 
 
 def setup_decode(wl, torch, ds, dev):

@@ -57,7 +57,8 @@ _SIGS = {
     "topk_select": ([_p, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i64, _i32, _i32,
                      _i32, _p, _p, _p], _i32),
     "sparse_mla_prefill": ([_p, _i32, _p, _i32, _p, _i64, _p, _i32, _i32, _i32, _i32,
-                            _i32, _f32, _p, _i32, _p, _p], _i32),
+                            _i32, _f32, _p, _i32, _p, _p, _sz, _p], _i32),
+    "sparse_mla_prefill_workspace_size": ([_i64, _i32], _sz),
     "sparse_mla_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
     "sparse_mla_decode": ([_p, _i32, _p, _i32, _p, _i64, _p, _i32, _i32, _i32, _i32,
                            _i32, _f32, _p, _i32, _p, _p, _sz, _p], _i32),
@@ -86,6 +87,9 @@ def _ptr(t):
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2}
 
 
 def dtype_code(t: torch.Tensor) -> int:
@@ -239,18 +243,27 @@ def _mla_common(q, kv, topk_idx, d_latent, out, out_dtype):
     return n_q, n_heads, d_qk - d_latent, out
 
 
+def sparse_mla_prefill_workspace_size(kv_rows: int, kv_dtype) -> int:
+    return lib.sparse_mla_prefill_workspace_size(kv_rows, _DTYPES[kv_dtype])
+
+
 def sparse_mla_prefill(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale=None,
                        out=None, out_dtype=None, lse=None, want_lse: bool = True,
-                       stream=None):
-    """Step 5 (prefill).  Returns (out [n_q, H, d_latent], lse [n_q, H] or None)."""
+                       workspace=None, stream=None):
+    """Step 5 (prefill).  Returns (out [n_q, H, d_latent], lse [n_q, H] or None).
+    fp8 kv needs a workspace (allocated here when not given)."""
     out_dtype = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
     n_q, H, d_rope, out = _mla_common(q, kv, topk_idx, d_latent, out, out_dtype)
     if want_lse and lse is None:
         lse = torch.empty((n_q, H), dtype=torch.float32, device=q.device)
+    need = sparse_mla_prefill_workspace_size(kv.shape[0], kv.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.sparse_mla_prefill(
         _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv), _ptr(kv_scale), kv.shape[0],
         _ptr(topk_idx), n_q, H, d_latent, d_rope, topk_idx.shape[1], sm_scale, _ptr(out),
-        dtype_code(out), _ptr(lse), _stream(stream))
+        dtype_code(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check("sparse_mla_prefill", st)
     return out, lse
 

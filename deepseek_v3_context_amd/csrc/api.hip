@@ -37,7 +37,7 @@ using namespace ds32cp;
 
 extern "C" {
 
-int32_t ds_abi_version(void) { return 1; }
+int32_t ds_abi_version(void) { return 2; }
 
 const char* ds_last_error(void) { return g_last_error.c_str(); }
 
@@ -246,16 +246,33 @@ static ds_status check_mla(const char* fn, const MlaArgs& a) {
   return DS_OK;
 }
 
+size_t sparse_mla_prefill_workspace_size(int64_t kv_rows, ds_dtype kv_dtype) {
+  if (kv_dtype != DS_FP8_E4M3FN || kv_rows <= 0) return 0;
+  return static_cast<size_t>(kv_rows) * kMlaWidenedRowBytes;
+}
+
 ds_status sparse_mla_prefill(const void* q, ds_dtype q_dtype, const void* kv,
                              ds_dtype kv_dtype, const float* kv_scale, int64_t kv_rows,
                              const int32_t* topk_idx, int32_t n_q, int32_t n_heads,
                              int32_t d_latent, int32_t d_rope, int32_t topk,
                              float sm_scale, void* out, ds_dtype out_dtype, float* lse,
-                             hipStream_t stream) {
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
   MlaArgs a{q, q_dtype, kv, kv_dtype, kv_scale, kv_rows, topk_idx, n_q, n_heads, d_latent,
             d_rope, topk, sm_scale, out, out_dtype, lse, 1, nullptr};
   ds_status st = check_mla("sparse_mla_prefill", a);
   if (st != DS_OK) return st;
+  const size_t need = sparse_mla_prefill_workspace_size(kv_rows, kv_dtype);
+  if (need > 0) {
+    DS_REQUIRE(ws != nullptr && ws_bytes >= need, DS_ERR_WORKSPACE,
+               "sparse_mla_prefill: fp8 kv needs sparse_mla_prefill_workspace_size() bytes of workspace");
+    DS_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, DS_ERR_INVALID_ARG,
+               "sparse_mla_prefill: workspace must be 256-byte aligned");
+    st = launch_widen_fp8_rows(kv, kv_scale, kv_rows, ws, stream);
+    if (st != DS_OK) return st;
+    a.kv = ws;
+    a.kv_dtype = DS_BF16;
+    a.kv_scale = nullptr;
+  }
   return launch_sparse_mla(a, stream);
 }
 

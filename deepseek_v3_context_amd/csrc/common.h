@@ -136,6 +136,10 @@ struct TopkArgs {
   int32_t n_seg = 0, seg_len = 0;
 };
 ds_status launch_topk(const TopkArgs& a, hipStream_t s);
+// fp8 latent rows (576 codes, scale per 128 rows) -> bf16 rows (code * scale)
+constexpr int kMlaWidenedRowBytes = 576 * 2;
+ds_status launch_widen_fp8_rows(const void* codes, const float* scale, int64_t rows, void* out,
+                                hipStream_t s);
 // Rows longer than this are selected in two phases when there are few of
 // them (their candidates need topk_two_phase_bytes() of workspace).
 constexpr int32_t kTopkSegLen = 8192;

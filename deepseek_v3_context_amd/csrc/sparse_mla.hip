@@ -1368,6 +1368,39 @@ static bool mla_transpose_reads() {
   return !(e && e[0] == '1');
 }
 
+// fp8 rows -> bf16 rows of code * scale (round to nearest even), 16 codes
+// per thread: one 16-byte load, two 16-byte stores.
+__global__ void __launch_bounds__(256)
+widen_fp8_rows_kernel(const uint8_t* codes, const float* scale, int64_t rows, uint16_t* out) {
+  constexpr int kPer = kMlaD / 16;   // 36 pieces of 16 codes per row
+  const int64_t piece = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (piece >= rows * kPer) return;
+  const int64_t r = piece / kPer;
+  const float sc = scale[r / kFp8BlockRows];
+  const uint4 v = *reinterpret_cast<const uint4*>(codes + piece * 16);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float2 lo = fp8x2_to_f32<false>(w[k]);
+    const float2 hi = fp8x2_to_f32<true>(w[k]);
+    o[2 * k] = f32_to_bf16_bits(lo.x * sc) | (static_cast<uint32_t>(f32_to_bf16_bits(lo.y * sc)) << 16);
+    o[2 * k + 1] = f32_to_bf16_bits(hi.x * sc) | (static_cast<uint32_t>(f32_to_bf16_bits(hi.y * sc)) << 16);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + piece * 16);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+ds_status launch_widen_fp8_rows(const void* codes, const float* scale, int64_t rows, void* out,
+                                hipStream_t s) {
+  if (rows <= 0) return DS_OK;
+  const int64_t pieces = rows * (kMlaD / 16);
+  widen_fp8_rows_kernel<<<static_cast<unsigned>(ceil_div(pieces, 256)), 256, 0, s>>>(
+      static_cast<const uint8_t*>(codes), scale, rows, static_cast<uint16_t*>(out));
+  return check_launch("sparse_mla (fp8 rows to bf16)");
+}
+
 int32_t mla_decode_splits(int32_t n_q, int32_t topk) {
   // enough workgroups to cover the 256 CUs; at least 4 tiles per split
   const int32_t tiles = static_cast<int32_t>(ceil_div(topk, kMlaTile));

@@ -68,7 +68,7 @@ typedef enum ds_status {
   DS_ERR_HIP = 4
 } ds_status;
 
-/* Version of this interface (bumped on any signature change). */
+/* Version of this interface (bumped on any signature change): 2. */
 int32_t ds_abi_version(void);
 
 /* Message describing the last error returned on the calling thread. */
@@ -224,18 +224,25 @@ ds_status topk_select(const float* scores, int64_t score_stride,
  * Supported: all-f32 path with n_heads <= 128, d_latent + d_rope <= 640;
  * bf16 q with bf16 or fp8 kv: n_heads % 32 == 0, n_heads <= 128,
  * d_latent == 512, d_rope == 64.  topk in [1, 2048].
+ * fp8 kv (prefill): the rows are first widened once per call into the
+ * caller's workspace as bf16 values code * scale (round to nearest even;
+ * relative error <= 2^-9 per element), and the bf16 path runs on them.
+ * ws [>= sparse_mla_prefill_workspace_size(kv_rows, kv_dtype) bytes] dev,
+ * 256-byte aligned; NULL is accepted when that size is 0 (bf16/f32 kv).
  * The decode variant splits each query's selected rows across workgroups
  * and merges the partial results by their log-sum-exp; it needs
  * ws_bytes >= sparse_mla_workspace_size(...).  Same results as the prefill
- * variant up to fp32 rounding.
+ * variant up to fp32 rounding (fp8 kv: it uses the codes exactly).
  * ------------------------------------------------------------------- */
+size_t sparse_mla_prefill_workspace_size(int64_t kv_rows, ds_dtype kv_dtype);
+
 ds_status sparse_mla_prefill(const void* q, ds_dtype q_dtype, const void* kv,
                              ds_dtype kv_dtype, const float* kv_scale,
                              int64_t kv_rows, const int32_t* topk_idx,
                              int32_t n_q, int32_t n_heads, int32_t d_latent,
                              int32_t d_rope, int32_t topk, float sm_scale,
                              void* out, ds_dtype out_dtype, float* lse,
-                             hipStream_t stream);
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 size_t sparse_mla_workspace_size(int32_t n_q, int32_t n_heads,
                                  int32_t d_latent, int32_t topk);

@@ -10,6 +10,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from oracle import round_robin_cp as rr
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_local_count():
-    assert ds.abi_version() == 1
+    assert ds.abi_version() == 2
     for T in (0, 1, 7, 8, 9, 8000, 25305, 65536):
         for cp in (1, 3, 8):
             for r in range(cp):
@@ -97,10 +98,17 @@ def test_indexer_rejects_unsupported_and_small_workspace():
 def test_mla_rejects_unsupported_dims_and_workspace():
     base = lambda q_dt, kv_dt, H, dl, dr, out_dt: (  # noqa: E731
         _p(), q_dt, _p(), kv_dt, None, 100, _p(), 4, H, dl, dr, 64, 0.1, _p(), out_dt, None)
-    assert lib.sparse_mla_prefill(*base(1, 1, 48, 512, 64, 1), None) == 2   # heads % 32
-    assert lib.sparse_mla_prefill(*base(1, 1, 128, 256, 64, 1), None) == 2  # latent dims
-    assert lib.sparse_mla_prefill(*base(0, 1, 16, 64, 16, 0), None) == 2    # f32 q, bf16 kv
-    assert lib.sparse_mla_prefill(*base(1, 2, 128, 512, 64, 1), None) == 1  # fp8 w/o scale
+    assert lib.sparse_mla_prefill(*base(1, 1, 48, 512, 64, 1), None, 0, None) == 2   # heads % 32
+    assert lib.sparse_mla_prefill(*base(1, 1, 128, 256, 64, 1), None, 0, None) == 2  # latent dims
+    assert lib.sparse_mla_prefill(*base(0, 1, 16, 64, 16, 0), None, 0, None) == 2    # f32 q, bf16 kv
+    assert lib.sparse_mla_prefill(*base(1, 2, 128, 512, 64, 1), None, 0, None) == 1  # fp8 w/o scale
+    # fp8 kv: the widened rows need workspace (checked before any launch)
+    fp8 = (_p(), 1, _p(), 2, _p(), 100, _p(), 4, 128, 512, 64, 64, 0.1, _p(), 1, None)
+    wneed = ds.sparse_mla_prefill_workspace_size(100, torch.float8_e4m3fn)
+    assert wneed == 100 * 576 * 2
+    assert lib.sparse_mla_prefill(*fp8, None, 0, None) == 3
+    assert lib.sparse_mla_prefill(*fp8, _p(), wneed - 1, None) == 3
+    assert ds.sparse_mla_prefill_workspace_size(100, torch.bfloat16) == 0
     need = ds.sparse_mla_workspace_size(4, 128, 512, 64)
     assert lib.sparse_mla_decode(*base(1, 1, 128, 512, 64, 1), _p(), need - 1, None) == 3
 
