@@ -133,15 +133,24 @@ __device__ __forceinline__ float head_sum(const f32x16 (&acc)[kIxRowBlocks],
 // gather of tile t+1 overlaps the MFMAs of tile t; every wave reads the
 // shared tile's B fragments from LDS.  Two waves per SIMD.
 constexpr int kIxPWaves = 8;
-constexpr int kIxPTile = 64;                       // keys per tile
+constexpr int kIxPTile = 128;                      // keys per tile (two 64-key halves)
+constexpr int kIxPHalf = 64;
 template <bool kFp8>
 struct IxTile {
   static constexpr int kRowBytes = kFp8 ? kIxDim : 2 * kIxDim;   // 128 / 256
+  static constexpr int kRowShift = kFp8 ? 7 : 8;
   static constexpr int kLdsRow = kRowBytes + 16;                  // padded
   static constexpr int kChunksPerRow = kLdsRow / 16;              // 9 / 17
-  static constexpr int kChunks = kIxPTile * kChunksPerRow;        // 576 / 1088
-  static constexpr int kInst = (kChunks + kWave - 1) / kWave;     // 9 / 17
+  static constexpr int kChunks = kIxPTile * kChunksPerRow;        // 1152 / 2176
+  static constexpr int kInst = kChunks / kWave;                   // 18 / 34
   static constexpr int kBytes = kInst * kWave * 16;               // LDS bytes per buffer
+  static constexpr int kPer = (kInst + kIxPWaves - 1) / kIxPWaves; // DMA slots per wave: 3 / 5
+  // instruction of slot i of a wave; past the last one, a repeat of the
+  // wave's previous instruction (identical bytes to the same place)
+  static __device__ __forceinline__ int inst(int wave, int i) {
+    const int m = wave + i * kIxPWaves;
+    return m < kInst ? m : m - kIxPWaves;
+  }
 };
 
 __shared__ __align__(16) uint8_t g_ix_buf0[IxTile<false>::kBytes];
@@ -152,22 +161,48 @@ __device__ __forceinline__ uint8_t* ix_buf() {
   return B ? g_ix_buf1 : g_ix_buf0;
 }
 
-// Gathers key rows [base, base + 64) into buffer B (rows past k_rows read
-// row 0; their scores are never stored).
+// Byte offset, within a tile's key rows, of the 16 bytes each lane of slot
+// i gathers (padding chunks re-read the row's last chunk).  Loop-invariant:
+// computed once per wave.
+template <bool kFp8>
+struct IxSlots {
+  using TL = IxTile<kFp8>;
+  uint32_t off[TL::kPer];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < TL::kPer; ++i) {
+      const int P = TL::inst(wave, i) * kWave + lane;
+      const int r = P / TL::kChunksPerRow;
+      const int c = P - r * TL::kChunksPerRow;
+      const int cc = c < TL::kRowBytes / 16 ? c : TL::kRowBytes / 16 - 1;
+      off[i] = static_cast<uint32_t>(r * TL::kRowBytes + cc * 16);
+    }
+  }
+};
+
+// Gathers key rows [base, base + 128) into buffer B: one DMA instruction per
+// slot, SGPR base + the slot's constant offsets.  Rows at or past k_rows
+// (the last tile of the key set) read the tile's first row instead; their
+// scores are never stored.  The instructions are not visible to the
+// compiler: the kernel waits for them itself before the tile barrier.
 template <int B, bool kFp8>
 __device__ __forceinline__ void ix_issue_tile(const uint8_t* keys, int64_t k_rows, int64_t base,
-                                              int wave, int lane) {
+                                              const IxSlots<kFp8>& sl, int wave) {
   using TL = IxTile<kFp8>;
-  for (int m = wave; m < TL::kInst; m += kIxPWaves) {
-    const int P = m * kWave + lane;
-    const int r = P / TL::kChunksPerRow;
-    const int c = P - r * TL::kChunksPerRow;
-    int64_t row = base + r;
-    row = (row < k_rows && r < kIxPTile) ? row : 0;
-    const int cc = c < TL::kRowBytes / 16 ? c : TL::kRowBytes / 16 - 1;
-    __builtin_amdgcn_global_load_lds(
-        keys + row * TL::kRowBytes + cc * 16,
-        (__attribute__((address_space(3))) void*)(ix_buf<B>() + m * kWave * 16), 16, 0, 0);
+  const uint8_t* src = keys + base * TL::kRowBytes;
+  const uint32_t lds = static_cast<uint32_t>(
+      (size_t)((__attribute__((address_space(3))) uint8_t*)ix_buf<B>()));
+  const bool full = base + kIxPTile <= k_rows;
+  const uint32_t rows_valid = static_cast<uint32_t>(k_rows - base);
+#pragma unroll
+  for (int i = 0; i < TL::kPer; ++i) {
+    uint32_t o = sl.off[i];
+    if (!full) o = (o >> TL::kRowShift) < rows_valid ? o : (o & (TL::kRowBytes - 1));
+    const uint32_t m0 = lds + static_cast<uint32_t>(TL::inst(wave, i) * kWave * 16);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(o), "s"(src), "s"(m0)
+                 : "memory", "m0");
   }
 }
 
@@ -192,8 +227,7 @@ constexpr int32_t kIxPChunkKeys = 2048;   // key rows per workgroup
 
 template <bool kFp8>
 __global__ void __launch_bounds__(kWave * kIxPWaves)
-indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks,
-                                 uint32_t grid) {
+indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks) {
   constexpr int32_t chunk_keys = kIxPChunkKeys;
   __shared__ int64_t q_lo[kIxPWaves], q_hi[kIxPWaves];
   // scores of the chunk stay in LDS until the end: a global store inside
@@ -240,10 +274,9 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
   rlo = rlo > c_lo ? rlo : c_lo;
   rhi = rhi < c_hi ? rhi : c_hi;
   if (rlo >= rhi) return;
-  const int64_t t_first = (rlo / kIxPTile) * kIxPTile;
+  const int64_t t_first = (rlo / kIxPHalf) * kIxPHalf;
   const int32_t n_tiles = static_cast<int32_t>(ceil_div(rhi - t_first, kIxPTile));
   const uint8_t* keys = static_cast<const uint8_t*>(a.k_idx);
-  ix_issue_tile<0, kFp8>(keys, a.k_rows, t_first, wave, lane);
 
   // this wave's query: A fragments, head weights of the rows this lane's
   // accumulator elements hold, causal range
@@ -265,6 +298,12 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
     }
   }
   float* srow = a.scores + static_cast<int64_t>(live ? j : 0) * a.score_stride;
+  IxSlots<kFp8> sl;
+  sl.init(wave, lane);
+  // query loads complete before any gather is in flight (a wait for them
+  // inside the tile loop would also wait for the gathers)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  ix_issue_tile<0, kFp8>(keys, a.k_rows, t_first, sl, wave);
 
   auto step = [&](auto bufc, int t) {
     constexpr int B = decltype(bufc)::value;
@@ -273,44 +312,51 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
     __builtin_amdgcn_s_barrier();         // every wave's; tile t-1 fully consumed
     asm volatile("" ::: "memory");
     const int64_t base = t_first + static_cast<int64_t>(t) * kIxPTile;
-    if (t + 1 < n_tiles) ix_issue_tile<1 - B, kFp8>(keys, a.k_rows, base + kIxPTile, wave, lane);
-    if (!live || base >= my_hi || base + kIxPTile <= my_lo) return;
-    const uint8_t* tile = ix_buf<B>();
-    // both 32-key column blocks at once: four independent accumulator
-    // chains per wave keep the MFMA pipe busy
-    f32x16 acc[2][kIxRowBlocks];
+    if (t + 1 < n_tiles) ix_issue_tile<1 - B, kFp8>(keys, a.k_rows, base + kIxPTile, sl, wave);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int hf = 0; hf < 2; ++hf) {
+      const int64_t hbase = base + hf * kIxPHalf;
+      if (!live || hbase >= my_hi || hbase + kIxPHalf <= my_lo) continue;
+      const uint8_t* tile = ix_buf<B>() + hf * kIxPHalf * IxTile<kFp8>::kLdsRow;
+      // both 32-key column blocks at once: four independent accumulator
+      // chains per wave keep the MFMA pipe busy
+      f32x16 acc[2][kIxRowBlocks];
 #pragma unroll
-      for (int rb = 0; rb < kIxRowBlocks; ++rb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[nb][rb][i] = 0.f;
-    bf16x8 b0 = ix_bfrag<kFp8>(tile, 0, 0, lane), b1 = ix_bfrag<kFp8>(tile, 1, 0, lane);
+        for (int rb = 0; rb < kIxRowBlocks; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < kIxKSteps; ++ks) {
-      bf16x8 n0 = b0, n1 = b1;
-      if (ks + 1 < kIxKSteps) {
-        n0 = ix_bfrag<kFp8>(tile, 0, ks + 1, lane);
-        n1 = ix_bfrag<kFp8>(tile, 1, ks + 1, lane);
+          for (int i = 0; i < 16; ++i) acc[nb][rb][i] = 0.f;
+      bf16x8 b0 = ix_bfrag<kFp8>(tile, 0, 0, lane), b1 = ix_bfrag<kFp8>(tile, 1, 0, lane);
+#pragma unroll
+      for (int ks = 0; ks < kIxKSteps; ++ks) {
+        bf16x8 n0 = b0, n1 = b1;
+        if (ks + 1 < kIxKSteps) {
+          n0 = ix_bfrag<kFp8>(tile, 0, ks + 1, lane);
+          n1 = ix_bfrag<kFp8>(tile, 1, ks + 1, lane);
+        }
+#pragma unroll
+        for (int rb = 0; rb < kIxRowBlocks; ++rb) {
+          acc[0][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b0, acc[0][rb], 0, 0, 0);
+          acc[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b1, acc[1][rb], 0, 0, 0);
+        }
+        b0 = n0;
+        b1 = n1;
       }
 #pragma unroll
-      for (int rb = 0; rb < kIxRowBlocks; ++rb) {
-        acc[0][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b0, acc[0][rb], 0, 0, 0);
-        acc[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b1, acc[1][rb], 0, 0, 0);
+      for (int nb = 0; nb < 2; ++nb) {
+        float v = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < kIxRowBlocks; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], fmaxf(acc[nb][rb][i], 0.f), v);
+        // the other half of the heads sits in lanes l^32
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                         false, false);
+        v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int64_t row = hbase + nb * 32 + (lane & 31);
+        if (lane < 32 && row >= my_lo && row < my_hi) sc[wave][row - c_lo] = v;
       }
-      b0 = n0;
-      b1 = n1;
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float v = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < kIxRowBlocks; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], fmaxf(acc[nb][rb][i], 0.f), v);
-      v += __shfl_xor(v, 32);
-      const int64_t row = base + nb * 32 + (lane & 31);
-      if (lane < 32 && row >= my_lo && row < my_hi) sc[wave][row - c_lo] = v;
     }
   };
   for (int32_t t = 0; t < n_tiles; t += 2) {
@@ -428,10 +474,10 @@ ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
   const uint32_t grid = static_cast<uint32_t>(round_up(static_cast<int64_t>(n_qblocks) * n_chunks, 8));
   if (fp8)
     indexer_prefill_pipelined_kernel<true><<<grid, kWave * kIxPWaves, 0, s>>>(
-        a, n_qblocks, n_chunks, grid);
+        a, n_qblocks, n_chunks);
   else
     indexer_prefill_pipelined_kernel<false><<<grid, kWave * kIxPWaves, 0, s>>>(
-        a, n_qblocks, n_chunks, grid);
+        a, n_qblocks, n_chunks);
   return check_launch("indexer_scores (prefill)");
 }
 
