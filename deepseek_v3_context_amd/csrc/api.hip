@@ -24,6 +24,18 @@ ds_status check_launch(const char* what) {
   return DS_OK;
 }
 
+int32_t device_cu_count() {
+  static int32_t cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 static bool is_act_dtype(ds_dtype d) { return d == DS_F32 || d == DS_BF16; }
 
 }  // namespace ds32cp

@@ -17,12 +17,16 @@ ds_status fail(ds_status code, const std::string& msg);
 // Checks the launch that just happened on the calling thread.
 ds_status check_launch(const char* what);
 
+// Compute units of the current device (cached per device).
+int32_t device_cu_count();
+
 // ----------------------------------------------------------- vector types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kFp8BlockRows = 128;

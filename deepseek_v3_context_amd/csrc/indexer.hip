@@ -376,76 +376,240 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
 }
 
 // ----------------------------------------------------- decode, MFMA path
-constexpr int kIxDecodeChunk = kIxWaves * 64;   // positions per workgroup
+// Work unit: 32 consecutive positions of one query (one MFMA N block).  The
+// units of all queries, in query order, are split evenly over the resident
+// waves (about two workgroups per CU), so every wave streams the same number
+// of key rows whatever the mix of context lengths.  A wave walks its units
+// query by query: the query's A fragments (64 VGPRs) and the 32 head
+// weights its lanes reduce are loaded once per query, and the key fragments
+// of the next unit are in flight while the current one runs its MFMAs.
+// Physical rows are resolved through the page table one unit further
+// ahead.  Every key row is read from HBM exactly once.
+constexpr int kIxDUnit = 32;
+
+__device__ __forceinline__ int64_t ix_units(const IndexerArgs& a, int32_t q) {
+  return ceil_div(clamp_len(a, q), kIxDUnit);
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int64_t o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// lane `l`'s value, as a wave-uniform (scalar) value
+__device__ __forceinline__ int64_t lane_value(int64_t v, int l) {
+  const int64_t x = __shfl(v, l);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 template <bool kFp8>
-__global__ void __launch_bounds__(256)
-indexer_paged_mfma_kernel(IndexerArgs a, int32_t n_chunks) {
-  __shared__ float wl[kIxHeads];
-  const int32_t j = blockIdx.x / n_chunks;
-  const int32_t chunk = blockIdx.x - j * n_chunks;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  if (j >= a.n_q) return;
-  const int32_t L = clamp_len(a, j);
-  const int64_t pos0 = static_cast<int64_t>(chunk) * kIxDecodeChunk;
-  if (pos0 >= L) return;
-  if (tid < kIxHeads) wl[tid] = a.w[static_cast<int64_t>(j) * kIxHeads + tid];
-  __syncthreads();
-  const int64_t wpos = pos0 + wave * 64;
-  if (wpos >= L) return;
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+indexer_paged_mfma_kernel(IndexerArgs a) {
+  constexpr int kRowBytes = kFp8 ? kIxDim : 2 * kIxDim;
+  const int lane = threadIdx.x & 63;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kIxWaves + (threadIdx.x >> 6);
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * kIxWaves;
 
-  const int32_t req = a.q_req ? a.q_req[j] : 0;
-  const int64_t kv0 = a.kv_start[j];
-  const uint16_t* q0 = static_cast<const uint16_t*>(a.q_idx) +
-                       static_cast<int64_t>(j) * kIxHeads * kIxDim;
-  bf16x8 qa[kIxRowBlocks][kIxKSteps];
-#pragma unroll
-  for (int rb = 0; rb < kIxRowBlocks; ++rb)
-#pragma unroll
-    for (int ks = 0; ks < kIxKSteps; ++ks) qa[rb][ks] = load_q_frag(q0, rb, ks, lane);
-
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int64_t p = wpos + nb * 32 + (lane & 31);
-    const int64_t row = p < L ? index_key_row(a, req, kv0 + p) : -1;
-    bf16x8 kb[kIxKSteps];
-#pragma unroll
-    for (int ks = 0; ks < kIxKSteps; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row >= 0) {
-        if constexpr (kFp8) {
-          const uint2 c = *reinterpret_cast<const uint2*>(
-              static_cast<const uint8_t*>(a.k_idx) + row * kIxDim + ks * 16 + (lane >> 5) * 8);
-          const uint2 lo = fp8x4_to_bf16x4(c.x);
-          const uint2 hi = fp8x4_to_bf16x4(c.y);
-          v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-          v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_idx) +
-                                              row * kIxDim + ks * 16 + (lane >> 5) * 8);
-        }
-      }
-      kb[ks] = __builtin_bit_cast(bf16x8, v);
+  // ---- this wave's units [u0, u1) and the query holding u0.  Lane l sums
+  // the units of queries [l*nb, (l+1)*nb); the lane whose block holds u0
+  // is then scanned query by query.
+  const int32_t nb = (a.n_q + kWave - 1) / kWave;
+  int64_t mine = 0;
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t q = lane * nb + i;
+    if (q < a.n_q) mine += ix_units(a, q);
+  }
+  const int64_t incl = wave_incl_scan(mine, lane);
+  const int64_t total = lane_value(incl, kWave - 1);
+  const int64_t u0 = g * total / n_waves, u1 = (g + 1) * total / n_waves;
+  if (u0 >= u1) return;   // no workgroup barrier in this kernel
+  const int l0 = static_cast<int>(__builtin_ctzll(__ballot(incl > u0)));
+  int64_t base = lane_value(incl - mine, l0);   // units before query j
+  int32_t j = -1;
+  for (int32_t c = 0; c < nb && j < 0; c += kWave) {
+    const int32_t q = l0 * nb + c + lane;
+    const int64_t n = (c + lane < nb && q < a.n_q) ? ix_units(a, q) : 0;
+    const int64_t inc = wave_incl_scan(n, lane);
+    const uint64_t hit = __ballot(base + inc > u0);
+    if (hit != 0ull) {
+      const int l = static_cast<int>(__builtin_ctzll(hit));
+      j = l0 * nb + c + l;
+      base += lane_value(inc - n, l);
+    } else {
+      base += lane_value(inc, kWave - 1);
     }
-    f32x16 acc[kIxRowBlocks];
+  }
+
+  const uint8_t* keys = static_cast<const uint8_t*>(a.k_idx);
+  __shared__ __align__(16) uint8_t tiles[kIxWaves][kFp8 ? 16 : 32 * 256];
+  uint8_t* tile = tiles[threadIdx.x >> 6];
+  for (int64_t u = u0; u < u1 && j < a.n_q; ++j) {
+    const int32_t L = clamp_len(a, j);
+    const int64_t nj = ceil_div(L, kIxDUnit);
+    const int64_t s_begin = u - base;
+    const int64_t s_end = nj < u1 - base ? nj : u1 - base;
+    base += nj;
+    if (s_begin >= s_end) continue;
+    u = base - nj + s_end;
+    float* srow = a.scores + static_cast<int64_t>(j) * a.score_stride;
+    const int32_t req = a.q_req ? a.q_req[j] : 0;
+    if (a.k_rows == 0 || req < 0 || req >= a.n_req) {   // every position unmapped
+      for (int64_t p = kIxDUnit * s_begin + lane; p < kIxDUnit * s_end && p < L; p += kWave)
+        srow[p] = -INFINITY;
+      continue;
+    }
+    const int64_t kv0 = a.kv_start[j];
+    const int32_t* table = a.page_table + static_cast<int64_t>(req) * a.max_pages;
+    const uint32_t ps = static_cast<uint32_t>(a.page_size);
+    // Page lookup of this lane's key in unit s, in two halves: the table
+    // load is issued one unit before the row is formed from it, so that the
+    // wait for it falls after the MFMAs of the unit in between.  Positions
+    // are int32 by interface, so 32-bit division is exact.
+    struct PageRef { int32_t pid; uint32_t off; bool ok; };
+    auto pt_issue = [&](int64_t s) -> PageRef {
+      const int64_t p = kIxDUnit * s + (lane & 31);
+      const int64_t l = kv0 + p;
+      const uint32_t pg = static_cast<uint32_t>(l) / ps;
+      const bool ok = p < L && l >= 0 && pg < static_cast<uint32_t>(a.max_pages);
+      return {table[ok ? pg : 0u], static_cast<uint32_t>(l) - pg * ps, ok};
+    };
+    auto row_from = [&](const PageRef& r) -> int64_t {
+      const int64_t row = static_cast<int64_t>(r.pid) * ps + r.off;
+      return (r.ok && r.pid >= 0 && row < a.k_rows) ? row : -1;
+    };
+
+    const uint16_t* q0 = static_cast<const uint16_t*>(a.q_idx) +
+                         static_cast<int64_t>(j) * kIxHeads * kIxDim;
+    bf16x8 qa[kIxRowBlocks][kIxKSteps];
 #pragma unroll
     for (int rb = 0; rb < kIxRowBlocks; ++rb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+      for (int ks = 0; ks < kIxKSteps; ++ks) qa[rb][ks] = load_q_frag(q0, rb, ks, lane);
+    // output element i of row block rb in this lane belongs to head
+    // 32*rb + 8*(i/4) + 4*(lane/32) + i%4
+    float wr[kIxRowBlocks][16];
+    const float* wj = a.w + static_cast<int64_t>(j) * kIxHeads;
 #pragma unroll
-    for (int ks = 0; ks < kIxKSteps; ++ks)
+    for (int rb = 0; rb < kIxRowBlocks; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wr[rb][i] = wj[rb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
+
+    // Key loads of one unit.  bf16: instruction i brings 8 whole 128-byte
+    // lines, half i%2 of keys (l%8) + 8*(i/2) (lane l takes 16 bytes), so
+    // that every request is a full line; the rows are then transposed
+    // through this wave's LDS tile into MFMA fragments.  fp8 (128-byte
+    // rows): lane l loads its fragment bytes of key l%32 directly.
+    // Unmapped keys read row 0 and are masked on write.
+    auto issue = [&](int64_t row, u32x4 (&kf)[kIxKSteps]) {
+      if constexpr (kFp8) {
+        const uint8_t* kp = keys + (row >= 0 ? row : 0) * kRowBytes + (lane >> 5) * 8;
+#pragma unroll
+        for (int ks = 0; ks < kIxKSteps; ++ks) {
+          const uint2 c = *reinterpret_cast<const uint2*>(kp + ks * 16);
+          kf[ks] = u32x4{c.x, c.y, 0u, 0u};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kIxKSteps; ++i) {
+          const int64_t r = __shfl(row, (lane & 7) + 8 * (i >> 1));
+          const uint8_t* kp = keys + (r >= 0 ? r : 0) * kRowBytes + 16 * (lane >> 3) + 128 * (i & 1);
+          kf[i] = *reinterpret_cast<const u32x4*>(kp);
+        }
+      }
+    };
+    auto step = [&](int64_t s, const u32x4 (&kf)[kIxKSteps], int64_t row) {
+      bf16x8 kb[kIxKSteps];
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int ks = 0; ks < kIxKSteps; ++ks) {
+          const uint2 lo = fp8x4_to_bf16x4(kf[ks].x);
+          const uint2 hi = fp8x4_to_bf16x4(kf[ks].y);
+          kb[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
+      } else {
+        // tile: key r's 16-byte chunk c at r*256 + 16*(c ^ swz(r)); the
+        // swizzle keeps both the line-shaped writes and the fragment reads
+        // (16 lanes, 16 keys, one chunk) on distinct banks
+        auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+#pragma unroll
+        for (int i = 0; i < kIxKSteps; ++i) {
+          const int r = (lane & 7) + 8 * (i >> 1);
+          const int c = 8 * (i & 1) + (lane >> 3);
+          *reinterpret_cast<u32x4*>(tile + r * 256 + 16 * (c ^ swz(r))) = kf[i];
+        }
+        const int r = lane & 31;
+#pragma unroll
+        for (int ks = 0; ks < kIxKSteps; ++ks) {
+          const int c = 2 * ks + (lane >> 5);
+          kb[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + r * 256 + 16 * (c ^ swz(r))));
+        }
+      }
+      f32x16 acc[kIxRowBlocks];
 #pragma unroll
       for (int rb = 0; rb < kIxRowBlocks; ++rb)
-        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], kb[ks], acc[rb], 0, 0, 0);
-    float v = head_sum(acc, wl, lane);
-    if (lane < 32 && p < L) {
-      if (row < 0) {
-        v = -INFINITY;
-      } else if constexpr (kFp8) {
-        v *= a.k_scale[row / kFp8BlockRows];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kIxKSteps; ++ks)
+#pragma unroll
+        for (int rb = 0; rb < kIxRowBlocks; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], kb[ks], acc[rb], 0, 0, 0);
+      float v = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < kIxRowBlocks; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v = fmaf(wr[rb][i], fmaxf(acc[rb][i], 0.f), v);
+      v += __shfl_xor(v, 32);
+      const int64_t p = kIxDUnit * s + lane;
+      if (lane < 32 && p < L) {
+        if (row < 0) {
+          v = -INFINITY;
+        } else if constexpr (kFp8) {
+          v *= a.k_scale[row / kFp8BlockRows];
+        }
+        srow[p] = v;
       }
-      a.scores[static_cast<int64_t>(j) * a.score_stride + p] = v;
+    };
+
+    // The key loads of unit u+1 are in flight while unit u computes; the
+    // table loads run four units ahead of the key loads, so that the row
+    // of the next unit is known (its table load long done) when its key
+    // loads are issued.  Loads are issued unconditionally (past the last
+    // unit they repeat it, from cache) so that every wait is the same in
+    // every iteration.
+    const int64_t s_last = s_end - 1;
+    auto cl = [&](int64_t u) { return u < s_last ? u : s_last; };
+    u32x4 k0[kIxKSteps], k1[kIxKSteps];
+    int64_t r0 = row_from(pt_issue(s_begin)), r1;
+    PageRef pa = pt_issue(cl(s_begin + 1)), pb = pt_issue(cl(s_begin + 2)),
+            pc = pt_issue(cl(s_begin + 3)), pd = pt_issue(cl(s_begin + 4));
+    issue(r0, k0);
+    for (int64_t s = s_begin; s < s_end; s += 4) {
+      r1 = row_from(pa);
+      pa = pt_issue(cl(s + 5));
+      issue(r1, k1);
+      step(s, k0, r0);
+      if (s + 1 >= s_end) break;
+      r0 = row_from(pb);
+      pb = pt_issue(cl(s + 6));
+      issue(r0, k0);
+      step(s + 1, k1, r1);
+      if (s + 2 >= s_end) break;
+      r1 = row_from(pc);
+      pc = pt_issue(cl(s + 7));
+      issue(r1, k1);
+      step(s + 2, k0, r0);
+      if (s + 3 >= s_end) break;
+      r0 = row_from(pd);
+      pd = pt_issue(cl(s + 8));
+      issue(r0, k0);
+      step(s + 3, k1, r1);
     }
   }
 }
@@ -463,10 +627,13 @@ ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
   }
   const bool fp8 = a.k_dtype == DS_FP8_E4M3FN;
   if (a.page_table != nullptr) {
-    const int32_t n_chunks = static_cast<int32_t>(ceil_div(a.max_kv_len, kIxDecodeChunk));
-    const int64_t blocks = static_cast<int64_t>(a.n_q) * n_chunks;
-    if (fp8) indexer_paged_mfma_kernel<true><<<blocks, 256, 0, s>>>(a, n_chunks);
-    else indexer_paged_mfma_kernel<false><<<blocks, 256, 0, s>>>(a, n_chunks);
+    // about two resident workgroups per CU, at least a few units per wave
+    const int64_t units_max = static_cast<int64_t>(a.n_q) * ceil_div(a.max_kv_len, kIxDUnit);
+    int64_t blocks = 2 * static_cast<int64_t>(device_cu_count());
+    const int64_t by_work = ceil_div(units_max, 4 * kIxWaves);
+    blocks = by_work < blocks ? by_work : blocks;
+    if (fp8) indexer_paged_mfma_kernel<true><<<blocks, kWave * kIxWaves, 0, s>>>(a);
+    else indexer_paged_mfma_kernel<false><<<blocks, kWave * kIxWaves, 0, s>>>(a);
     return check_launch("indexer_scores (paged)");
   }
   const int32_t n_qblocks = static_cast<int32_t>(ceil_div(a.n_q, kIxPWaves));

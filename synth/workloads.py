@@ -119,6 +119,10 @@ _add(Workload("small_prefill_topk2048", "prefill", seed=12,
 _add(Workload("small_decode_paged", "decode", seed=13, n_req=5, len_lo=40,
               len_hi=3000, topk=256, page_size=64,
               description="5 requests, lengths in [40, 3000], top-k 256"))
+_add(Workload("small_decode_paged_fp8", "decode", seed=14, n_req=6, len_lo=40,
+              len_hi=5000, topk=256, page_size=64, kv_fmt="fp8",
+              description="6 requests, lengths in [40, 5000], top-k 256; latent"
+                          " KV and indexer keys e4m3fn, per-128-row scale"))
 _add(replace(WORKLOADS["tiny_prefill_t256_cp4"], name="tiny_prefill_dense",
              seed=20, topk=256,
              description="tiny prefill with top-k >= context: dense causal"))

@@ -98,17 +98,19 @@ def run_decode(wl, inp: dict, want_scores: bool = True) -> dict:
     q_idx = to_dev(inp["q_idx"], wl.act_fmt)
     w = torch.from_numpy(inp["w"]).to(DEV)
     q = to_dev(inp["q"], wl.act_fmt)
+    kv_scale = None if inp["kv_scale"] is None else torch.from_numpy(inp["kv_scale"]).to(DEV)
+    ki_scale = None if inp["k_idx_scale"] is None else torch.from_numpy(inp["k_idx_scale"]).to(DEV)
     max_len = int(inp["lengths"].max())
     idx, score = ds.indexer_topk(q_idx, w, ki, meta["kv_start"], meta["kv_len"], max_len,
                                  wl.topk, q_req=meta["q_req"], page_table=table,
-                                 page_size=wl.page_size, want_score=True)
-    out, lse = ds.sparse_mla_decode(q, kv, idx, wl.scale, wl.d_latent)
+                                 page_size=wl.page_size, k_scale=ki_scale, want_score=True)
+    out, lse = ds.sparse_mla_decode(q, kv, idx, wl.scale, wl.d_latent, kv_scale=kv_scale)
     res = {}
     if want_scores:
         res["scores"] = ds.indexer_scores(q_idx, w, ki, meta["kv_start"], meta["kv_len"],
                                           max_len, q_req=meta["q_req"], page_table=table,
-                                          page_size=wl.page_size)
-    out_p, lse_p = ds.sparse_mla_prefill(q, kv, idx, wl.scale, wl.d_latent)
+                                          page_size=wl.page_size, k_scale=ki_scale)
+    out_p, lse_p = ds.sparse_mla_prefill(q, kv, idx, wl.scale, wl.d_latent, kv_scale=kv_scale)
     torch.cuda.synchronize()
     say(f"[gpu] decode {wl.name}: done")
     res.update({"topk_idx": idx.cpu().numpy(), "topk_score": score.cpu().numpy(),

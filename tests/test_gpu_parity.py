@@ -161,6 +161,10 @@ def test_decode_small_all_rows():
     _check_decode("small_decode_paged", all_rows=True)
 
 
+def test_decode_small_fp8_all_rows():
+    _check_decode("small_decode_paged_fp8", all_rows=True)
+
+
 def test_decode_full_size_all_requests():
     _check_decode("decode_32req_paged", all_rows=True)
 
