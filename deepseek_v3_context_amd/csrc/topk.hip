@@ -63,14 +63,15 @@ __device__ __forceinline__ uint32_t tk_block_scan(uint32_t v, int lane, int wave
 
 // kMode 0: one workgroup selects a whole row.
 // kMode 1 (two-phase, first phase): workgroup (row, s) selects the top-k of
-//   positions [s*seg_len, (s+1)*seg_len) of its row and writes them, in
-//   position order and padded to k entries (score -inf, position -1), to
-//   the row's candidate list.  The row's top-k is a subset of the union of
-//   its segments' top-k (ties included: a segment keeps its lowest
-//   positions among equal scores), so nothing is lost.
+//   positions [s*seg_len, (s+1)*seg_len) of its row and writes them (score
+//   and position), in position order and padded to k entries (score -inf,
+//   position -1), to the row's candidate list.  The row's top-k is a
+//   subset of the union of its segments' top-k (ties included: a segment
+//   keeps its lowest positions among equal scores), so nothing is lost.
 // kMode 2 (second phase): one workgroup selects the row's top-k from its
 //   n_seg*k candidates, which are in position order; padding scores are
-//   -inf, below every real (finite) indexer score.
+//   -inf, below every finite score (a key scored -inf is an unmapped one,
+//   whose row is -1 like a padding entry's, so ties there change nothing).
 template <int kTkThreads, int kMode>
 __global__ void __launch_bounds__(kTkThreads)
 topk_kernel(TopkArgs a, int32_t cache_keys) {
@@ -79,6 +80,7 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   __shared__ uint32_t hist[kTkWaves][256];   // one histogram per wave (less contention)
   __shared__ uint32_t sh_digit, sh_remaining;
   __shared__ uint32_t wave_tot[kTkWaves];
+  __shared__ int32_t sel_t[kTopkMax];        // selected elements in output order (kMode 0, 2)
 
   const int32_t j = kMode == 1 ? static_cast<int32_t>(blockIdx.x / a.n_seg) : blockIdx.x;
   const int32_t seg = kMode == 1 ? static_cast<int32_t>(blockIdx.x % a.n_seg) : 0;
@@ -103,20 +105,28 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
     row_scores = a.cand_score + cbase;
     if (L > a.topk) L = a.n_seg * a.topk;
   }
-  // logical position (within the row) of element t, -1 for padding
-  auto pos_of = [&](int32_t t) -> int64_t {
-    if constexpr (kMode == 2) return a.cand_pos[cbase + t];
-    return pos0 + t;
+  // What element t contributes: in the first phase of the two-phase
+  // selection its logical position (the candidates keep position order,
+  // and only the final k are mapped); otherwise its output row, the
+  // physical KV row of its position (-1 when unmapped or padding).
+  auto row_of = [&](int32_t t) -> int32_t {
+    if constexpr (kMode == 1) {
+      return pos0 + t;
+    } else if constexpr (kMode == 2) {
+      const int32_t p = a.cand_pos[cbase + t];
+      return p >= 0 ? static_cast<int32_t>(topk_key_row(a, req, kv0 + p)) : -1;
+    } else {
+      return static_cast<int32_t>(topk_key_row(a, req, kv0 + t));
+    }
   };
-  // the slot-th selected element (position order) is element t
-  auto emit = [&](uint32_t slot, int32_t t, float score) {
+  // the slot-th selected element (position order) contributes `v`
+  auto emit = [&](uint32_t slot, int32_t v, float score) {
     if constexpr (kMode == 1) {
       const int64_t c = cbase + static_cast<int64_t>(seg) * a.topk + slot;
       a.cand_score[c] = score;
-      a.cand_pos[c] = static_cast<int32_t>(pos_of(t));
+      a.cand_pos[c] = v;
     } else {
-      const int64_t p = pos_of(t);
-      out_idx[slot] = p >= 0 ? static_cast<int32_t>(topk_key_row(a, req, kv0 + p)) : -1;
+      out_idx[slot] = v;
       if (out_score) out_score[slot] = score;
     }
   };
@@ -124,7 +134,7 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   if (L <= a.topk) {  // every key is selected
     for (int32_t t = tid; t < a.topk; t += kTkThreads) {
       if (t < L) {
-        emit(t, t, row_scores[t]);
+        emit(t, row_of(t), row_scores[t]);
       } else if constexpr (kMode == 1) {
         const int64_t c = cbase + static_cast<int64_t>(seg) * a.topk + t;
         a.cand_score[c] = -INFINITY;
@@ -281,13 +291,26 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
 #pragma unroll
       for (int k = 0; k < kTkPer; ++k) {
         if ((take >> k) & 1u) {
-          if (slot < static_cast<uint32_t>(a.topk)) emit(slot, b0 + t0 + k, order_key_to_float(u[k]));
+          if (slot < static_cast<uint32_t>(a.topk)) {
+            if constexpr (kMode == 1) emit(slot, row_of(b0 + t0 + k), order_key_to_float(u[k]));
+            else sel_t[slot] = b0 + t0 + k;
+          }
           ++slot;
         }
       }
       taken += take_total;
       eq_seen += eq_total;
       if (taken >= static_cast<uint32_t>(a.topk)) break;   // uniform: all threads agree
+    }
+  }
+  if constexpr (kMode != 1) {
+    // map the selected elements to rows with every lookup in flight at
+    // once (a lookup may be two dependent loads: candidate position, then
+    // page table)
+    __syncthreads();
+    for (int32_t s = tid; s < a.topk; s += kTkThreads) {
+      const int32_t t = sel_t[s];
+      emit(s, row_of(t), order_key_to_float(float_order_key(row_scores[t])));
     }
   }
 }
