@@ -128,6 +128,31 @@ constexpr int kMlaRowBytes = kMlaD * 2;           // 1152 (bf16 row)
 constexpr int kMlaRowChunks = kMlaRowBytes / 16;  // 72
 constexpr int kMlaLdsRow = kMlaRowBytes + 16;     // padded LDS row stride
 
+// ---- split partials (decode): O unnormalised in bf16 [n_q, n_splits, H,
+// Dl], then (m, l) in fp32 [n_q, n_splits, H, 2] from a 256-byte boundary
+__host__ __device__ inline size_t mla_partial_o_bytes(int64_t n_q, int64_t n_splits,
+                                                      int64_t n_heads) {
+  return static_cast<size_t>(round_up(n_q * n_splits * n_heads * kMlaDl * 2, 256));
+}
+__device__ __forceinline__ uint16_t* mla_partial_o(const MlaArgs& a, int32_t j, int32_t split,
+                                                   int32_t h) {
+  return static_cast<uint16_t*>(a.ws) +
+         ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * kMlaDl;
+}
+__device__ __forceinline__ float* mla_partial_ml(const MlaArgs& a, int32_t j, int32_t split,
+                                                 int32_t h) {
+  return reinterpret_cast<float*>(static_cast<uint8_t*>(a.ws) +
+                                  mla_partial_o_bytes(a.n_q, a.n_splits, a.n_heads)) +
+         ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * 2;
+}
+// four consecutive fp32 outputs -> four bf16 (round to nearest even)
+__device__ __forceinline__ void mla_store_bf16x4(uint16_t* p, float x0, float x1, float x2, float x3) {
+  uint2 pk;
+  pk.x = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
+  pk.y = f32_to_bf16_bits(x2) | (static_cast<uint32_t>(f32_to_bf16_bits(x3)) << 16);
+  *reinterpret_cast<uint2*>(p) = pk;
+}
+
 // Byte offset of 16-byte chunk `c` of tile row `r`.  The 16-byte pad makes
 // consecutive rows start 36 banks apart, so 16 lanes reading one chunk of
 // 16 consecutive rows (K fragments) and 16 lanes reading 4 rows x 32 bytes
@@ -371,18 +396,12 @@ mla_mfma_kernel(MlaArgs a, int32_t keys_per_split) {
         a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
             l_run[g2] > 0.f ? (m_ref[g2] + log2f(l_run[g2])) * kLn2 : -INFINITY;
     } else {
-      // partials: O (unnormalised, fp32) [n_q, n_splits, H, Dl]; (m, l) [.., 2]
-      float* po = static_cast<float*>(a.ws) +
-                  ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * kMlaDl +
-                  grp * 4;
+      uint16_t* po = mla_partial_o(a, j, split, h) + grp * 4;
 #pragma unroll
       for (int cb = 0; cb < kMlaCBlocks; ++cb)
-        *reinterpret_cast<float4*>(po + cb * 16) =
-            make_float4(o[g2][cb][0], o[g2][cb][1], o[g2][cb][2], o[g2][cb][3]);
+        mla_store_bf16x4(po + cb * 16, o[g2][cb][0], o[g2][cb][1], o[g2][cb][2], o[g2][cb][3]);
       if (grp == 0) {
-        float* pml = static_cast<float*>(a.ws) +
-                     static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl +
-                     ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * 2;
+        float* pml = mla_partial_ml(a, j, split, h);
         pml[0] = m_ref[g2];
         pml[1] = l_run[g2];
       }
@@ -836,12 +855,10 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
                           o[cb][hg][3] * inv);
       }
     } else {
-      float* po = static_cast<float*>(a.ws) +
-                  ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * kMlaDl + col0;
+      uint16_t* po = mla_partial_o(a, j, split, h) + col0;
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb)
-        *reinterpret_cast<float4*>(po + cb * 16) =
-            make_float4(o[cb][hg][0], o[cb][hg][1], o[cb][hg][2], o[cb][hg][3]);
+        mla_store_bf16x4(po + cb * 16, o[cb][hg][0], o[cb][hg][1], o[cb][hg][2], o[cb][hg][3]);
     }
   }
   if (lane < 16) {
@@ -850,9 +867,7 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
         a.lse[static_cast<int64_t>(j) * a.n_heads + h_own] =
             l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : -INFINITY;
     } else {
-      float* pml = static_cast<float*>(a.ws) +
-                   static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl +
-                   ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h_own) * 2;
+      float* pml = mla_partial_ml(a, j, split, h_own);
       pml[0] = m_ref;
       pml[1] = l_run;
     }
@@ -1293,12 +1308,10 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
                           o[cb][hg][3] * inv);
       }
     } else {
-      float* po = static_cast<float*>(a.ws) +
-                  ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * kMlaDl + col0;
+      uint16_t* po = mla_partial_o(a, j, split, h) + col0;
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb)
-        *reinterpret_cast<float4*>(po + cb * 16) =
-            make_float4(o[cb][hg][0], o[cb][hg][1], o[cb][hg][2], o[cb][hg][3]);
+        mla_store_bf16x4(po + cb * 16, o[cb][hg][0], o[cb][hg][1], o[cb][hg][2], o[cb][hg][3]);
     }
   }
   if (lane < 16) {
@@ -1310,9 +1323,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
           a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
               l_run[hb] > 0.f ? (m_ref[hb] + log2f(l_run[hb])) * kLn2 : -INFINITY;
       } else {
-        float* pml = static_cast<float*>(a.ws) +
-                     static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl +
-                     ((static_cast<int64_t>(j) * a.n_splits + split) * a.n_heads + h) * 2;
+        float* pml = mla_partial_ml(a, j, split, h);
         pml[0] = m_ref[hb];
         pml[1] = l_run[hb];
       }
@@ -1322,27 +1333,40 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
 
 // Merge split partials: one workgroup per (query, head), one thread per
 // output column pair.
+constexpr int kMlaMaxSplits = 16;   // topk <= 2048 rows, at least 4 tiles per split
+
 __global__ void __launch_bounds__(256)
 mla_combine_kernel(MlaArgs a) {
   const int32_t j = blockIdx.x;
   const int32_t h = blockIdx.y;
   const int tid = threadIdx.x;
-  const float* pml = static_cast<const float*>(a.ws) +
-                     static_cast<int64_t>(a.n_q) * a.n_splits * a.n_heads * kMlaDl;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s)
-    M = fmaxf(M, pml[((static_cast<int64_t>(j) * a.n_splits + s) * a.n_heads + h) * 2]);
-  float Lsum = 0.f;
-  float acc0 = 0.f, acc1 = 0.f;
   const int c = tid * 2;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const int64_t ph = (static_cast<int64_t>(j) * a.n_splits + s) * a.n_heads + h;
-    const float ms = pml[ph * 2];
-    const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    Lsum += pml[ph * 2 + 1] * wgt;
-    const float2 v = *reinterpret_cast<const float2*>(static_cast<const float*>(a.ws) + ph * kMlaDl + c);
-    acc0 = fmaf(v.x, wgt, acc0);
-    acc1 = fmaf(v.y, wgt, acc1);
+  // every split's (m, l) and this thread's two columns, all loads in flight
+  float ms[kMlaMaxSplits], ls[kMlaMaxSplits];
+  uint32_t v[kMlaMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMlaMaxSplits; ++s) {
+    if (s < a.n_splits) {
+      const float* pml = mla_partial_ml(a, j, s, h);
+      ms[s] = pml[0];
+      ls[s] = pml[1];
+      v[s] = *reinterpret_cast<const uint32_t*>(mla_partial_o(a, j, s, h) + c);
+    } else {
+      ms[s] = -INFINITY;
+      ls[s] = 0.f;
+      v[s] = 0u;
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMlaMaxSplits; ++s) M = fmaxf(M, ms[s]);
+  float Lsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMlaMaxSplits; ++s) {
+    const float wgt = ms[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[s] - M);
+    Lsum += ls[s] * wgt;
+    acc0 = fmaf(bf16_bits_to_f32(static_cast<uint16_t>(v[s] & 0xffffu)), wgt, acc0);
+    acc1 = fmaf(bf16_bits_to_f32(static_cast<uint16_t>(v[s] >> 16)), wgt, acc1);
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + c;
@@ -1406,14 +1430,16 @@ int32_t mla_decode_splits(int32_t n_q, int32_t topk) {
   const int32_t tiles = static_cast<int32_t>(ceil_div(topk, kMlaTile));
   int32_t want = static_cast<int32_t>(ceil_div(256, n_q > 0 ? n_q : 1));
   int32_t max_splits = tiles / 4 > 0 ? tiles / 4 : 1;
+  max_splits = max_splits < kMlaMaxSplits ? max_splits : kMlaMaxSplits;   // the combine's bound
   want = want < max_splits ? want : max_splits;
   return want > 0 ? want : 1;
 }
 
 size_t mla_partials_bytes(int32_t n_q, int32_t n_heads, int32_t d_latent,
                           int32_t n_splits) {
-  return sizeof(float) * static_cast<size_t>(n_q) * n_splits * n_heads *
-         (static_cast<size_t>(d_latent) + 2);
+  (void)d_latent;   // the kernels that split handle d_latent == kMlaDl only
+  return mla_partial_o_bytes(n_q, n_splits, n_heads) +
+         sizeof(float) * 2 * static_cast<size_t>(n_q) * n_splits * n_heads;
 }
 
 ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
