@@ -15,13 +15,13 @@
 // weight) is 32 in-register FMAs plus one cross-half swap.
 //   * prefill: a workgroup of 8 waves owns 8 consecutive queries (one per
 //     wave, A fragments and head weights in registers for the whole chunk)
-//     and a chunk of absolute key rows; 64-key tiles are gathered into LDS
-//     by DMA, double-buffered, and shared by the 8 waves.  Queries of one
-//     workgroup may belong to different requests: each masks its own
-//     causal range on write.
-//   * decode: keys are paged per request, so a workgroup owns one query
-//     and 256 logical positions (64 per wave) and reads B fragments
-//     straight from HBM (each key row is read exactly once).
+//     and a chunk of absolute key rows; key tiles (128 bf16 or 256 fp8
+//     rows) are gathered into LDS by DMA, double-buffered, and shared by
+//     the 8 waves.  Queries of one workgroup may belong to different
+//     requests: each masks its own causal range on write.
+//   * decode: keys are paged per request; units of 32 positions are split
+//     evenly over the resident waves, and each key row is read from HBM
+//     exactly once (bf16 rows through a per-wave LDS transpose).
 // fp8 keys are widened to bf16 exactly; the per-block scale is positive
 // and multiplies the whole score of its key (ReLU commutes with a
 // positive factor), so it is applied once per key after the head sum.
@@ -128,23 +128,25 @@ __device__ __forceinline__ float head_sum(const f32x16 (&acc)[kIxRowBlocks],
 // --------------------------------------------- prefill, pipelined path
 // A workgroup of 8 waves owns 8 consecutive queries (one per wave: A
 // fragments in 64 VGPRs, the 64 head weights of the query in 32 VGPRs) and
-// a chunk of absolute key rows.  64-key tiles are gathered straight into
-// LDS with global_load_lds_dwordx4 (no VGPRs), double-buffered so that the
+// a chunk of absolute key rows.  Key tiles (128 bf16 or 256 fp8 rows) are
+// gathered straight into LDS with global_load_lds_dwordx4 (no VGPRs),
+// double-buffered so that the
 // gather of tile t+1 overlaps the MFMAs of tile t; every wave reads the
 // shared tile's B fragments from LDS.  Two waves per SIMD.
 constexpr int kIxPWaves = 8;
-constexpr int kIxPTile = 128;                      // keys per tile (two 64-key halves)
-constexpr int kIxPHalf = 64;
+constexpr int kIxPHalf = 64;                       // keys per MFMA pass (two 32-key blocks)
 template <bool kFp8>
 struct IxTile {
+  // keys per tile: 256 fp8 rows or 128 bf16 rows (about 36 KB of LDS)
+  static constexpr int kTile = kFp8 ? 256 : 128;
   static constexpr int kRowBytes = kFp8 ? kIxDim : 2 * kIxDim;   // 128 / 256
   static constexpr int kRowShift = kFp8 ? 7 : 8;
   static constexpr int kLdsRow = kRowBytes + 16;                  // padded
   static constexpr int kChunksPerRow = kLdsRow / 16;              // 9 / 17
-  static constexpr int kChunks = kIxPTile * kChunksPerRow;        // 1152 / 2176
-  static constexpr int kInst = kChunks / kWave;                   // 18 / 34
+  static constexpr int kChunks = kTile * kChunksPerRow;           // 2304 / 2176
+  static constexpr int kInst = kChunks / kWave;                   // 36 / 34
   static constexpr int kBytes = kInst * kWave * 16;               // LDS bytes per buffer
-  static constexpr int kPer = (kInst + kIxPWaves - 1) / kIxPWaves; // DMA slots per wave: 3 / 5
+  static constexpr int kPer = (kInst + kIxPWaves - 1) / kIxPWaves; // DMA slots per wave: 5 / 5
   // instruction of slot i of a wave; past the last one, a repeat of the
   // wave's previous instruction (identical bytes to the same place)
   static __device__ __forceinline__ int inst(int wave, int i) {
@@ -153,8 +155,10 @@ struct IxTile {
   }
 };
 
-__shared__ __align__(16) uint8_t g_ix_buf0[IxTile<false>::kBytes];
-__shared__ __align__(16) uint8_t g_ix_buf1[IxTile<false>::kBytes];
+constexpr int kIxBufBytes = IxTile<true>::kBytes > IxTile<false>::kBytes ? IxTile<true>::kBytes
+                                                                         : IxTile<false>::kBytes;
+__shared__ __align__(16) uint8_t g_ix_buf0[kIxBufBytes];
+__shared__ __align__(16) uint8_t g_ix_buf1[kIxBufBytes];
 
 template <int B>
 __device__ __forceinline__ uint8_t* ix_buf() {
@@ -192,7 +196,7 @@ __device__ __forceinline__ void ix_issue_tile(const uint8_t* keys, int64_t k_row
   const uint8_t* src = keys + base * TL::kRowBytes;
   const uint32_t lds = static_cast<uint32_t>(
       (size_t)((__attribute__((address_space(3))) uint8_t*)ix_buf<B>()));
-  const bool full = base + kIxPTile <= k_rows;
+  const bool full = base + TL::kTile <= k_rows;
   const uint32_t rows_valid = static_cast<uint32_t>(k_rows - base);
 #pragma unroll
   for (int i = 0; i < TL::kPer; ++i) {
@@ -234,6 +238,7 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
   // the tile loop would make every wait for the next tile's gather
   // (vmcnt counts stores too) also wait for the store to retire
   __shared__ float sc[kIxPWaves][chunk_keys];
+  __shared__ float ksc[chunk_keys / kFp8BlockRows];   // fp8 key scales of the chunk
   // Every workgroup reads the same key rows (the whole indexer key set of
   // a prefill fits in each XCD's L2), so workgroups are left in the
   // hardware's round-robin order over the XCDs, which spreads the causal
@@ -260,6 +265,12 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
     q_lo[tid] = lo;
     q_hi[tid] = hi;
   }
+  if constexpr (kFp8) {
+    if (tid < chunk_keys / kFp8BlockRows) {
+      const int64_t r0 = static_cast<int64_t>(chunk) * chunk_keys + tid * kFp8BlockRows;
+      ksc[tid] = r0 < a.k_rows ? a.k_scale[r0 / kFp8BlockRows] : 0.f;
+    }
+  }
   __syncthreads();
   int64_t rlo = INT64_MAX, rhi = 0;
 #pragma unroll
@@ -275,7 +286,8 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
   rhi = rhi < c_hi ? rhi : c_hi;
   if (rlo >= rhi) return;
   const int64_t t_first = (rlo / kIxPHalf) * kIxPHalf;
-  const int32_t n_tiles = static_cast<int32_t>(ceil_div(rhi - t_first, kIxPTile));
+  constexpr int kTile = IxTile<kFp8>::kTile;
+  const int32_t n_tiles = static_cast<int32_t>(ceil_div(rhi - t_first, kTile));
   const uint8_t* keys = static_cast<const uint8_t*>(a.k_idx);
 
   // this wave's query: A fragments, head weights of the rows this lane's
@@ -311,10 +323,10 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();         // every wave's; tile t-1 fully consumed
     asm volatile("" ::: "memory");
-    const int64_t base = t_first + static_cast<int64_t>(t) * kIxPTile;
-    if (t + 1 < n_tiles) ix_issue_tile<1 - B, kFp8>(keys, a.k_rows, base + kIxPTile, sl, wave);
+    const int64_t base = t_first + static_cast<int64_t>(t) * kTile;
+    if (t + 1 < n_tiles) ix_issue_tile<1 - B, kFp8>(keys, a.k_rows, base + kTile, sl, wave);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < kTile / kIxPHalf; ++hf) {
       const int64_t hbase = base + hf * kIxPHalf;
       if (!live || hbase >= my_hi || hbase + kIxPHalf <= my_lo) continue;
       const uint8_t* tile = ix_buf<B>() + hf * kIxPHalf * IxTile<kFp8>::kLdsRow;
@@ -369,7 +381,7 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
     const int64_t hi = my_hi < c_hi ? my_hi : c_hi;
     for (int64_t r = lo + lane; r < hi; r += kWave) {
       float v = sc[wave][r - c_lo];
-      if constexpr (kFp8) v *= a.k_scale[r / kFp8BlockRows];   // per-row fp8 scale
+      if constexpr (kFp8) v *= ksc[(r - c_lo) / kFp8BlockRows];   // per-row fp8 scale
       srow[r - my_lo] = v;
     }
   }
