@@ -354,6 +354,11 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
         }
         b0 = n0;
         b1 = n1;
+        // bf16: one k-step per scheduling region, so that the compiler
+        // does not regroup the products into dependent chains across steps
+        // (the four products of a step go to four different accumulators).
+        // fp8 keeps the free schedule, which overlaps the conversions.
+        if constexpr (!kFp8) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
