@@ -264,6 +264,55 @@ def test_decode_page_boundaries():
         assert set(gi[j][gi[j] >= 0].tolist()) == set(s["topk_idx"][s["topk_idx"] >= 0].tolist())
 
 
+@pytest.mark.parametrize("kfmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("ps", [1, 16, 48, 64])
+def test_decode_indexer_page_sizes_and_offsets(ps, kfmt):
+    # Paged indexer scores and top-k with page sizes that do and do not
+    # divide the 32-position work unit, queries whose causal range starts
+    # inside the request (kv_start > 0), and lengths around unit edges.
+    lengths = np.array([1, 31, 32, 33, 700, 2500], dtype=np.int32)
+    kv_start = np.array([0, 3, 0, 40, 17, 0], dtype=np.int32)
+    span = lengths + kv_start
+    pages = [-(-int(x) // ps) for x in span]
+    rng = np.random.default_rng(100 + ps)
+    perm = rng.permutation(sum(pages)).astype(np.int32)
+    table = np.full((lengths.size, max(pages)), -1, dtype=np.int32)
+    off = 0
+    for i, k in enumerate(pages):
+        table[i, :k] = perm[off: off + k]
+        off += k
+    rows = sum(pages) * ps
+    from synth.draw import to_bf16_bits, to_e4m3fn_blocks
+    ki = (rng.standard_normal((rows, 128)) / np.sqrt(128)).astype(np.float32)
+    ki_v, ki_scale = (to_bf16_bits(ki), None) if kfmt == "bf16" else to_e4m3fn_blocks(ki)
+    qi_b = to_bf16_bits((rng.standard_normal((lengths.size, 64, 128)) / np.sqrt(128)).astype(np.float32))
+    w = (rng.standard_normal((lengths.size, 64)) / 8).astype(np.float32)
+    meta = {"q_req": np.arange(lengths.size, dtype=np.int32), "kv_start": kv_start, "kv_len": lengths}
+    dev = {k: torch.from_numpy(v).to(gp.DEV) for k, v in meta.items()}
+    ks_dev = None if ki_scale is None else torch.from_numpy(ki_scale).to(gp.DEV)
+    args = (gp.to_dev(qi_b, "bf16"), torch.from_numpy(w).to(gp.DEV), gp.to_dev(ki_v, kfmt),
+            dev["kv_start"], dev["kv_len"], int(lengths.max()))
+    paging = dict(q_req=dev["q_req"], page_table=torch.from_numpy(table).to(gp.DEV), page_size=ps)
+    sc = ds.indexer_scores(*args, k_scale=ks_dev, **paging)
+    idx, _ = ds.indexer_topk(*args, 16, k_scale=ks_dev, **paging)
+    torch.cuda.synchronize()
+    sc, gi = sc.cpu().numpy(), idx.cpu().numpy()
+    sel = opl.indexer_topk_rows(range(lengths.size), meta, qi_b, "bf16", w, ki_v, kfmt, ki_scale, 16,
+                                page_table=table, page_size=ps)
+    for j, s in enumerate(sel):
+        L = int(lengths[j])
+        assert np.all(np.abs(sc[j, :L] - s["scores64"]) <= SCORE_ATOL), f"row {j}: score error"
+        got = set(gi[j][gi[j] >= 0].tolist())
+        exp = set(s["topk_idx"][s["topk_idx"] >= 0].tolist())
+        if L <= 16:
+            assert got == exp, f"row {j}: must select every causal key"
+        else:
+            pos_of = {int(x): p for p, x in enumerate(s["key_rows"].tolist())}
+            kth = s["scores64"][s["sel_pos"][-1]]
+            far = [x for x in got ^ exp if abs(s["scores64"][pos_of[x]] - kth) > TOPK_BAND]
+            assert not far, f"row {j}: selections outside the tie band"
+
+
 def test_integer_outputs_repeatable():
     wl = get("small_prefill_3req_cp4")
     n = orr.local_count(wl.num_tokens, wl.cp_size, wl.cp_rank)
