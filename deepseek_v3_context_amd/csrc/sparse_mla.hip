@@ -1271,7 +1271,10 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
     exact = true;
   }
 
-  // ---- epilogue: owners publish (m, l); every wave writes its columns
+  // ---- epilogue: owners publish (m, l).  O goes out through the tile
+  // buffers (free now), a block of heads at a time, so that the global
+  // stores are whole head rows: a lane's own fragments would make every
+  // store instruction cover 16 heads x 32 bytes of partly written lines.
   if (lane < 16) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -1279,41 +1282,67 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       sh.l_fin[h0 + 16 * hb] = l_run[hb];
     }
   }
-  __syncthreads();
+  __syncthreads();   // also: every wave is done with the tile buffers
   const int col0 = wave * kCols + grp * 4;
+  auto write_out = [&](auto esz) {
+    constexpr int kE = decltype(esz)::value;         // bytes per element: 2 (bf16) or 4
+    constexpr int kRowB = kMlaDl * kE;               // one head row of O
+    constexpr int kStride = kRowB + 16;              // padded stage row (banks)
+    constexpr int kCH0 = kE == 2 ? 64 : 32;
+    constexpr int kCH = kCH0 < kHeads ? kCH0 : kHeads;   // heads per block
+    static_assert(kCH * kStride <= 3 * kPipeTileBytes, "a block fits in the tile buffers");
+    uint8_t* stage = g_mla_bufs;
 #pragma unroll
-  for (int hg = 0; hg < kHG; ++hg) {
-    const int h = hg * 16 + li;
-    const float lf = sh.l_fin[h];
-    if (a.n_splits == 1) {
-      const float inv = lf > 0.f ? 1.f / lf : 0.f;
-      const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + col0;
-      if (a.out_dtype == DS_BF16) {
-        uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
+    for (int c = 0; c < kHeads / kCH; ++c) {
+#pragma unroll
+      for (int hq = 0; hq < kCH / 16; ++hq) {
+        const int hg = c * (kCH / 16) + hq;
+        float sc = 1.f;   // split partials stay unnormalised
+        if (a.n_splits == 1) {
+          const float lf = sh.l_fin[hg * 16 + li];
+          sc = lf > 0.f ? 1.f / lf : 0.f;
+        }
+        uint8_t* srow = stage + (hq * 16 + li) * kStride + col0 * kE;
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) {
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(o[cb][hg][0] * inv) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][1] * inv)) << 16);
-          pk.y = f32_to_bf16_bits(o[cb][hg][2] * inv) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][3] * inv)) << 16);
-          *reinterpret_cast<uint2*>(out + cb * 16) = pk;
+          if constexpr (kE == 2) {
+            uint2 pk;
+            pk.x = f32_to_bf16_bits(o[cb][hg][0] * sc) |
+                   (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][1] * sc)) << 16);
+            pk.y = f32_to_bf16_bits(o[cb][hg][2] * sc) |
+                   (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][3] * sc)) << 16);
+            *reinterpret_cast<uint2*>(srow + cb * 16 * kE) = pk;
+          } else {
+            *reinterpret_cast<float4*>(srow + cb * 16 * kE) =
+                make_float4(o[cb][hg][0] * sc, o[cb][hg][1] * sc, o[cb][hg][2] * sc, o[cb][hg][3] * sc);
+          }
         }
-      } else {
-        float* out = static_cast<float*>(a.out) + obase;
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
-          *reinterpret_cast<float4*>(out + cb * 16) =
-              make_float4(o[cb][hg][0] * inv, o[cb][hg][1] * inv, o[cb][hg][2] * inv,
-                          o[cb][hg][3] * inv);
       }
-    } else {
-      uint16_t* po = mla_partial_o(a, j, split, h) + col0;
-#pragma unroll
-      for (int cb = 0; cb < kCB; ++cb)
-        mla_store_bf16x4(po + cb * 16, o[cb][hg][0], o[cb][hg][1], o[cb][hg][2], o[cb][hg][3]);
+      // LDS-only barriers: waiting for the global stores to retire (as a
+      // full __syncthreads would) is not needed to reuse the stage
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      constexpr int kPieces = kRowB / 16;   // 16-byte pieces per head row
+      for (int i = tid; i < kCH * kPieces; i += kThreads) {
+        const int r = i / kPieces, q = i - r * kPieces;
+        const int h = c * kCH + r;
+        uint8_t* dst = a.n_splits == 1
+                           ? static_cast<uint8_t*>(a.out) +
+                                 (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl * kE
+                           : reinterpret_cast<uint8_t*>(mla_partial_o(a, j, split, h));
+        *reinterpret_cast<uint4*>(dst + q * 16) =
+            *reinterpret_cast<const uint4*>(stage + r * kStride + q * 16);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // the next block reuses the stage
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
-  }
+  };
+  if (a.n_splits == 1 && a.out_dtype != DS_BF16) write_out(std::integral_constant<int, 4>{});
+  else write_out(std::integral_constant<int, 2>{});
   if (lane < 16) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
