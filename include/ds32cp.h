@@ -231,8 +231,10 @@ ds_status topk_select(const float* scores, int64_t score_stride,
  * 256-byte aligned; NULL is accepted when that size is 0 (bf16/f32 kv).
  * The decode variant splits each query's selected rows across workgroups
  * and merges the partial results by their log-sum-exp; it needs
- * ws_bytes >= sparse_mla_workspace_size(...).  Same results as the prefill
- * variant up to fp32 rounding (fp8 kv: it uses the codes exactly).
+ * ws_bytes >= sparse_mla_workspace_size(...).  The partial outputs are
+ * held in bf16 (their maxima and sums in fp32), so its results match the
+ * prefill variant's up to one bf16 rounding of each partial (relative
+ * error <= 2^-9) (fp8 kv: it uses the codes exactly).
  * ------------------------------------------------------------------- */
 size_t sparse_mla_prefill_workspace_size(int64_t kv_rows, ds_dtype kv_dtype);
 
