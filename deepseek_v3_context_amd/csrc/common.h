@@ -53,14 +53,14 @@ __device__ __forceinline__ float2 fp8x2_to_f32(uint32_t word) {
   return make_float2(r.x, r.y);
 }
 
-// Four e4m3fn codes -> four bfloat16 bit patterns, exactly (every e4m3fn
-// value is representable in bfloat16, so truncating the float is exact).
+// Four e4m3fn codes -> four bfloat16 bit patterns, exactly: every e4m3fn
+// value is representable in bfloat16, and gfx950's packed conversion with a
+// unit scale gives those values (checked on the device against the two-step
+// conversion through fp32 for every code in every byte position).
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t word) {
-  float2 lo = fp8x2_to_f32<false>(word);
-  float2 hi = fp8x2_to_f32<true>(word);
   uint2 out;
-  out.x = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
-  out.y = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+  out.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+  out.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
   return out;
 }
 
