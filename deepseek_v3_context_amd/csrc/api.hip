@@ -234,6 +234,8 @@ static ds_status check_mla(const char* fn, const MlaArgs& a) {
   DS_REQUIRE(a.topk >= 1 && a.topk <= 2048, DS_ERR_INVALID_ARG, f + ": topk must be in [1, 2048]");
   DS_REQUIRE(a.n_heads >= 1 && a.d_latent >= 1 && a.d_rope >= 0, DS_ERR_INVALID_ARG,
              f + ": bad head/latent dims");
+  DS_REQUIRE(a.sm_scale > 0.f && a.sm_scale <= 3.4e38f, DS_ERR_INVALID_ARG,
+             f + ": sm_scale must be positive and finite");
   if (a.n_q > 0)
     DS_REQUIRE(a.q && a.topk_idx && a.out && (a.kv_rows == 0 || a.kv), DS_ERR_INVALID_ARG,
                f + ": NULL q/kv/topk_idx/out");

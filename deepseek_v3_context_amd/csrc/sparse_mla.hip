@@ -32,6 +32,7 @@
 #include <stdlib.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -874,6 +875,17 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
   }
 }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order:
+// a loop whose index is a constant expression in the body.
+template <class F, int... U>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, U...>) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // ------------------------------------------- bf16 KV, 32 heads per wave
 // One workgroup of kNW = n_heads/32 waves (one per SIMD) per (query, split
 // of its rows).  Wave w computes S^T for 32 heads (two 16-head MFMA blocks
@@ -910,46 +922,49 @@ __device__ __forceinline__ void mla_qk_settle(f32x4& a, f32x4& b, f32x4& c, f32x
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
-// Gather slots of the wide kernel with the address arithmetic taken out of
-// the tile loop: for each of this wave's slots, the lane's row slot in the
-// tile and byte column are packed into 16 bits (row << 11 | column), two
-// slots per register, computed once.  A slot is then one LDS read of the
-// row index, one multiply-add and the DMA instruction (SGPR base + 32-bit
-// offset: the latent KV must be smaller than 4 GiB).  One wave per SIMD
-// issues in order, so every instruction here delays its MFMAs.
-template <int kNW>
-struct WideGather {
-  static constexpr int kPer = MlaIssue<kNW>::kPer;
-  uint32_t info[(kPer + 1) / 2];
-  __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < kPer; i += 2) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (i + h < kPer) {
-          const int P = mla_gather_inst<kNW>(wave, i + h) * kWave + lane;
-          const int r = P / kDmaRowChunks;
-          const int c = P - r * kDmaRowChunks;
-          const uint32_t e = (static_cast<uint32_t>(r) << 11) |
-                             static_cast<uint32_t>((c < kMlaRowChunks ? c : kMlaRowChunks - 1) * 16);
-          v |= e << (16 * h);
-        }
-      }
-      info[i / 2] = v;
-    }
-  }
-  __device__ __forceinline__ int row_slot(int i) const { return (info[i / 2] >> (16 * (i & 1) + 11)) & 31; }
-  __device__ __forceinline__ uint32_t col(int i) const { return (info[i / 2] >> (16 * (i & 1))) & 2047; }
-};
+// Tile layout of the wide kernel: a 32-row tile is 36 column blocks of
+// 1 KB, block c holding bytes [32c, 32c+32) of all 32 rows as two halves
+// of 512 bytes (bytes [32c, 32c+16) of every row, then [32c+16, 32c+32));
+// within the second half the rows are permuted r -> r ^ 8.  One DMA
+// wave-instruction fills exactly one block (lane l lands at 16l: half
+// l >> 5, row (l & 31) ^ 8(l >> 5)), so every lane gathers from a single
+// row of the tile for all its instructions, and both the K fragment reads
+// (16 rows x 16 bytes per 16-lane group) and the transposed V reads (4
+// rows x 32 bytes) hit distinct banks.
+constexpr int kWideTileBytes = kPipeTile * kMlaRowBytes;         // 36864
+constexpr int kWideInst = kWideTileBytes / (kWave * 16);         // 36 blocks
+__device__ __forceinline__ int wide_off(int r, int x) {
+  const int hh = (x >> 4) & 1;
+  return (x >> 5) * 1024 + hh * 512 + (r ^ (hh << 3)) * 16 + (x & 15);
+}
+// per-lane byte offset of this lane's 16 bytes of K fragment (key block 0,
+// k-step 0); key block kb adds 256, k-step ks adds 2048
+__device__ __forceinline__ int wide_koff(int l) {
+  const int hh = (l >> 4) & 1;
+  return (l >> 5) * 1024 + hh * 512 + ((l & 15) ^ (hh << 3)) * 16;
+}
+// per-lane byte offset of the transposed V read (rows 4g + (li >> 2), the
+// 8-byte piece li & 3 of the 32-byte column block of output columns
+// [col0, col0 + 16)); column block +1 adds 1024, rows +16 add 256
+__device__ __forceinline__ int wide_voff(int l, int col0) {
+  const int li = l & 15, g = l >> 4, hh = (li >> 1) & 1;
+  return (col0 >> 4) * 1024 + hh * 512 + ((4 * g + (li >> 2)) ^ (hh << 3)) * 16 + (li & 1) * 8;
+}
+// tile row whose bytes lane l gathers
+__device__ __forceinline__ int wide_gather_slot(int l) { return (l & 31) ^ ((l >> 5) << 3); }
 
-// One DMA wave-instruction: 16 bytes of row `row` at byte column colb to
-// LDS address lds + 16*lane (lds: the instruction's chunk block in a tile
-// buffer, the same for the whole wave).
-__device__ __forceinline__ void wide_gather_issue(const uint8_t* kv, uint32_t lds, int32_t row,
-                                                  uint32_t colb) {
+// The global byte offset a lane gathers from for every DMA instruction of a
+// tile: its row (empty slots, -1, read row 0: their logits are masked and
+// their softmax weight is 0) and its half.  32-bit: the latent KV must be
+// smaller than 4 GiB.
+__device__ __forceinline__ uint32_t wide_gather_base(int32_t row, int l) {
   row = row < 0 ? 0 : row;
-  const uint32_t off = static_cast<uint32_t>(row) * kMlaRowBytes + colb;
+  return static_cast<uint32_t>(row) * kMlaRowBytes + static_cast<uint32_t>((l >> 5) << 4);
+}
+// One DMA wave-instruction: block m of the tile at LDS address lds (the
+// block's start: lane l lands at lds + 16l) from bytes [32m, 32m+32) of the
+// lane's row.
+__device__ __forceinline__ void wide_gather_issue(const uint8_t* kv, uint32_t lds, uint32_t off) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(off), "s"(kv), "s"(lds)
@@ -961,13 +976,13 @@ struct MlaWideShared {
   static constexpr int kHeads = 32 * kNW;
   uint4 qrope[2][4][kHeads];   // rope k-steps of Q^T: [ks-16][lane group][head]
   int32_t sidx[kMlaMaxKeys];
-  uint4 p[4][kHeads];          // P^T fragments: [lane group][head] -> 8 bf16
+  uint4 p[2][4][kHeads];       // P^T fragments: [tile parity][lane group][head] -> 8 bf16
   int32_t wave_cnt[kNW];       // index compaction scratch
   int32_t bail[kNW];           // wave w saw a tile beyond its reference + 2^kWideBail
   float m_fin[kHeads], l_fin[kHeads];
 };
 
-template <bool kTrV, int kNW>
+template <bool kTrV, int kNW, bool kLag>
 __global__ void __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   constexpr int kThreads = kWave * kNW;
@@ -976,7 +991,8 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   constexpr int kCols = kMlaDl / kNW;         // output columns per wave
   constexpr int kCB = kCols / 16;             // 16-column blocks per wave
   constexpr int kCBC = kCB < 4 ? kCB : 4;     // column blocks per PV chunk
-  constexpr int kPer = MlaIssue<kNW>::kPer;   // DMA wave-instructions per wave and tile
+  constexpr int kPer = kWideInst / kNW;      // DMA wave-instructions per wave and tile
+  static_assert(kPer * kNW == kWideInst, "the tile's blocks split evenly over the waves");
   constexpr int kQReg = kMlaDl / 32;          // latent k-steps of Q^T in VGPRs (16)
   __shared__ MlaWideShared<kNW> sh;
   // Names an accumulator register so that the compiler places the MFMA
@@ -1043,19 +1059,21 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
   const uint32_t lds_bufs = static_cast<uint32_t>(
       (size_t)((__attribute__((address_space(3))) uint8_t*)g_mla_bufs));
-  WideGather<kNW> gs;
-  gs.init(wave, lane);
-  // LDS address of slot i's chunk block in buffer b
+  // wave w issues blocks w, w + kNW, ...: slot i is block kNW*i + wave
   auto slot_lds = [&](int b, int i) {
-    return lds_bufs + static_cast<uint32_t>(b * kPipeTileBytes + mla_gather_inst<kNW>(wave, i) * kWave * 16);
+    return lds_bufs + static_cast<uint32_t>(b * kPipeTileBytes + (kNW * i + wave) * 1024);
+  };
+  auto slot_off = [&](uint32_t base, int i) { return base + static_cast<uint32_t>(32 * (kNW * i + wave)); };
+  auto row_of = [&](int t0) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    return wide_gather_base(sh.sidx[t0 + wide_gather_slot(ln)], ln);
   };
   // all of this wave's slots of the tile with rows sidx[t0..] into buffer b
   auto issue_tile = [&](int b, int t0) {
-    int32_t row[kMlaIssueMax];
+    const uint32_t base = row_of(t0);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) row[i] = sh.sidx[t0 + gs.row_slot(i)];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) wide_gather_issue(kv, slot_lds(b, i), row[i], gs.col(i));
+    for (int i = 0; i < kPer; ++i) wide_gather_issue(kv, slot_lds(b, i), slot_off(base, i));
   };
   // Q loads complete before any gather is in flight (a wait for them inside
   // the tile loop would also wait for the gathers)
@@ -1066,19 +1084,24 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   // head blocks), optionally issuing this wave's gather slots of another
   // tile (rows sidx[t0g..], into gbuf) spread over the k-steps
   auto qk = [&](const uint8_t* tile, f32x4 (&st)[2][2], bool gather, int t0g, int gb) {
+    // the gather's row is read first, so that waiting for it does not wait
+    // for the K fragment reads behind it
+    const uint32_t gbase = gather ? row_of(t0g) : 0u;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int koff = (ln & 15) * kPipeRow + (ln >> 4) * 16;
+    const int koff = wide_koff(ln);
     auto kfrag = [&](int kb, int ks) {
       return __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(tile + koff + kb * 16 * kPipeRow + ks * 64));
+          bf16x8, *reinterpret_cast<const uint4*>(tile + koff + kb * 256 + ks * 2048));
     };
-    int32_t grow = gather ? sh.sidx[t0g + gs.row_slot(0)] : 0;
     f32x4 su[2][2];
     // K fragments are read kAhead k-steps before their products; the
     // scheduling barriers keep the compiler from sinking the reads next to
     // their use (one wave per SIMD: nothing else hides the LDS latency)
     constexpr int kAhead = 2;
+    // k-steps over which the gather slots are spread: the lagged schedule
+    // gathers only one tile ahead, so its slots go out in the first half
+    constexpr int kSpread = kLag ? kMlaKSteps / 2 : kMlaKSteps;
     bf16x8 kf[kAhead + 1][2];
 #pragma unroll
     for (int s = 0; s < kAhead; ++s) {
@@ -1109,10 +1132,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       }
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        if (i * kMlaKSteps / kPer == ks && gather) {
-          wide_gather_issue(kv, slot_lds(gb, i), grow, gs.col(i));
-          if (i + 1 < kPer) grow = sh.sidx[t0g + gs.row_slot(i + 1)];
-        }
+        if (i * kSpread / kPer == ks && gather) wide_gather_issue(kv, slot_lds(gb, i), slot_off(gbase, i));
       }
     }
     mla_qk_settle(st[0][0], st[0][1], st[1][0], st[1][1]);
@@ -1144,6 +1164,139 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   bool exact = false;   // m_ref is the exact maximum (after a restart)
   f32x4 o[kCB][kHG];
   float l_run[2];
+
+  // ---- lagged schedule (kLag): the softmax of tile t runs interleaved
+  // with the PV products of tile t-1, so that its vector work (about 600
+  // clocks per tile, the 16 exponentials at quarter rate included) issues
+  // in the shadow of the matrix core.  One wave per SIMD issues in order
+  // and an MFMA holds the next one back for its 16 clocks, so the
+  // interleave has to be one product at a time: unit u (of 64) is a small
+  // piece of softmax followed by one PV product, with scheduling barriers
+  // between them so that the compiler keeps that order.
+  //   pv_c: issue the PV products of the previous tile (V in vtile, P^T in
+  //         parity buffer pb_rd); sm_c: run the softmax of st and write its
+  //         P^T to parity buffer pb_wr.  Softmax without PV is the first
+  //         tile, which also sets the reference maximum.
+  auto phase_b = [&](auto pv_c, auto sm_c, const uint8_t* vtile, int pb_rd, int pb_wr,
+                     f32x4 (&st)[2][2], bool& beyond) __attribute__((always_inline)) {
+    constexpr bool kPV = decltype(pv_c)::value;
+    constexpr bool kSM = decltype(sm_c)::value;
+    constexpr bool kFirst = !kPV;
+    constexpr int kCBL = kCB < 8 ? kCB : 8;   // column blocks whose V fragments are held
+    constexpr int kUnits = kCB * kHG;         // PV products per tile and wave
+    static_assert(kUnits == 64, "64 PV products per tile and wave");
+    static_assert(kCB == kCBL, "the lagged schedule holds every V fragment of the wave");
+    float mx[2], nm[2], psum[2] = {0.f, 0.f};
+    bf16x8 pvb[2];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int li_t = ln & 15, grp_t = ln >> 4;
+    const int voff = wide_voff(ln, wave * kCols);
+    bf16x8 vf[kCBL];
+    bf16x8 pf[2];
+    auto load_p = [&](int hg) {
+      return __builtin_bit_cast(bf16x8, sh.p[pb_rd][grp_t][hg * 16 + li_t]);
+    };
+    if constexpr (kPV) {
+#pragma unroll
+      for (int c = 0; c < kCBL; ++c) {
+        if constexpr (kTrV) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vtile + voff + c * 1024));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vtile + voff + 256 + c * 1024));
+          vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          const int x = (wave * kCols + c * 16 + li_t) * 2;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vf[c][i] = *reinterpret_cast<const __bf16*>(vtile + wide_off(4 * grp_t + i, x));
+            vf[c][4 + i] = *reinterpret_cast<const __bf16*>(vtile + wide_off(16 + 4 * grp_t + i, x));
+          }
+        }
+      }
+      pf[0] = load_p(0);
+    }
+    // softmax pieces; u is a compile-time constant once the unit loop is
+    // unrolled.  Values: st[kb][hb][i] is key 16kb + 4grp + i of head
+    // h0 + 16hb; v = 8hb + 4kb + i.
+    auto micro = [&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < 2) {                       // raw maximum of head block u
+        float m = fmaxf(fmaxf(st[0][u][0], st[0][u][1]), fmaxf(st[0][u][2], st[0][u][3]));
+        m = fmaxf(m, fmaxf(fmaxf(st[1][u][0], st[1][u][1]), fmaxf(st[1][u][2], st[1][u][3])));
+        mx[u] = m;
+      } else if constexpr (u == 2) {               // across the four 16-lane rows
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const auto a2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[hb]),
+                                                            __float_as_uint(mx[hb]), false, false);
+          mx[hb] = fmaxf(__uint_as_float(a2[0]), __uint_as_float(a2[1]));
+        }
+      } else if constexpr (u == 3) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const auto b2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx[hb]),
+                                                            __float_as_uint(mx[hb]), false, false);
+          mx[hb] = fmaxf(__uint_as_float(b2[0]), __uint_as_float(b2[1])) * scale2;
+        }
+      } else if constexpr (u == 4) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          if (kFirst && !exact) m_ref[hb] = mx[hb];
+          nm[hb] = -m_ref[hb];
+        }
+      } else if constexpr (u == 5) {
+        beyond = (mx[0] > m_ref[0] + kWideBail) || (mx[1] > m_ref[1] + kWideBail);
+      } else if constexpr (u < 6 + 3 * 16) {       // weights exp2(scale2 * s - m_ref), three steps per value
+        constexpr int v = (u - 6) / 3, ph = (u - 6) % 3;
+        constexpr int hb = v >> 3, kb = (v >> 2) & 1, i = v & 3;
+        if constexpr (ph == 0) {
+          st[kb][hb][i] = __builtin_fmaf(st[kb][hb][i], scale2, nm[hb]);
+        } else if constexpr (ph == 1) {
+          st[kb][hb][i] = __builtin_amdgcn_exp2f(st[kb][hb][i]);
+        } else {
+          psum[hb] += st[kb][hb][i];
+          if constexpr ((i & 1) != 0) {
+            pvb[hb][kb * 4 + i - 1] = static_cast<__bf16>(st[kb][hb][i - 1]);
+            pvb[hb][kb * 4 + i] = static_cast<__bf16>(st[kb][hb][i]);
+          }
+        }
+      } else if constexpr (u == 54) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const auto a2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum[hb]),
+                                                            __float_as_uint(psum[hb]), false, false);
+          psum[hb] = __uint_as_float(a2[0]) + __uint_as_float(a2[1]);
+        }
+      } else if constexpr (u == 55) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const auto b2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(psum[hb]),
+                                                            __float_as_uint(psum[hb]), false, false);
+          l_run[hb] += __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+        }
+      } else if constexpr (u == 56) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          sh.p[pb_wr][grp][h0 + 16 * hb] = __builtin_bit_cast(uint4, pvb[hb]);
+      } else if constexpr (u == 57) {
+        if (__ballot(beyond) != 0ull && lane == 0) sh.bail[wave] = 1;
+      }
+    };
+    static_for<kUnits>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (kSM) micro(uc);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kPV) {
+        constexpr int hg = u / kCBL, c = u % kCBL;
+        // the next head group's P^T fragment, read one group ahead
+        if constexpr (c == 0 && hg + 1 < kHG) pf[(hg + 1) & 1] = load_p(hg + 1);
+        o[c][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c], pf[hg & 1], o[c][hg], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
   for (;;) {
     if (exact) {
       // ---- first pass: exact maximum of every head over all rows (tiles
@@ -1171,8 +1324,79 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       for (int hg = 0; hg < kHG; ++hg) o[cb][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_run[0] = l_run[1] = 0.f;
     if (n_tiles > 0) issue_tile(0, 0);
-    if (n_tiles > 1) issue_tile(1, kPipeTile);
+    if (!kLag && n_tiles > 1) issue_tile(1, kPipeTile);
     bool bailed = false;
+    if constexpr (kLag) {
+      // tile t lives in buffer t mod 3; its gather was issued during QK of
+      // tile t-1.  One barrier per tile: tile t has landed, P^T of tile t-1
+      // and the bail flags of its softmax are visible, and every wave is
+      // done with PV of tile t-2, whose buffer takes the gather of t+1.
+      const std::true_type yes{};
+      const std::false_type no{};
+      // QK of tile t (buffer b) with the gather of tile t+1 spread through it
+      auto qk_tile = [&](int32_t t, int b, f32x4 (&st)[2][2]) __attribute__((always_inline)) {
+        const uint8_t* tile = g_mla_bufs + b * kPipeTileBytes;
+        qk(tile, st, t + 1 < n_tiles, (t + 1) * kPipeTile, b == 2 ? 0 : b + 1);
+        // valid rows are compacted to the front: only the last tile is
+        // partial; its missing keys get a logit of -inf (weight 0)
+        const int32_t rem = n_valid - t * kPipeTile;
+        if (rem < kPipeTile) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (kb * 16 + grp * 4 + i >= rem) st[kb][hb][i] = -INFINITY;
+        }
+      };
+      auto tile_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) lgkmcnt(0): this wave's gather and P^T writes
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      };
+      // the first tile (peeled: softmax alone, and it sets the reference)
+      if (n_tiles > 0) {
+        tile_barrier();
+        f32x4 st[2][2];
+        qk_tile(0, 0, st);
+        bool beyond = false;
+        phase_b(no, yes, g_mla_bufs, 0, 0, st, beyond);
+      }
+      for (int32_t t = 1, b = 1; t < n_tiles; ++t, b = b == 2 ? 0 : b + 1) {
+        tile_barrier();
+        bool bail = false;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) bail |= sh.bail[w] != 0;
+        if (bail) {
+          bailed = true;
+          break;
+        }
+        f32x4 st[2][2];
+        qk_tile(t, b, st);
+        bool beyond = false;
+        phase_b(yes, yes, g_mla_bufs + (b == 0 ? 2 : b - 1) * kPipeTileBytes,
+                (t - 1) & 1, t & 1, st, beyond);
+      }
+      if (!bailed && n_tiles > 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        bool bail = false;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) bail |= sh.bail[w] != 0;
+        if (bail) {
+          bailed = true;
+        } else {
+          f32x4 st[2][2];
+          bool beyond = false;
+          const int bl = (n_tiles - 1) % 3;
+          phase_b(yes, no, g_mla_bufs + bl * kPipeTileBytes, (n_tiles - 1) & 1, 0, st, beyond);
+        }
+      }
+    } else
     // tile t lives in buffer t mod 3; its gather was issued two tiles ahead
     for (int32_t t = 0, b = 0; t < n_tiles; ++t, b = b == 2 ? 0 : b + 1) {
       if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
@@ -1207,7 +1431,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
             pv[kb * 4 + i] = static_cast<__bf16>(pw);
           }
         l_run[hb] += mla_rows_sum(psum);
-        sh.p[grp][h0 + 16 * hb] = __builtin_bit_cast(uint4, pv);
+        sh.p[0][grp][h0 + 16 * hb] = __builtin_bit_cast(uint4, pv);
       }
       if (__ballot(beyond) != 0ull && lane == 0) sh.bail[wave] = 1;
       // P of every head and the bail flags visible to all waves; only LDS
@@ -1227,8 +1451,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
       const int li_t = ln & 15, grp_t = ln >> 4;
-      const int voff = (4 * grp_t + (li_t >> 2)) * kPipeRow + ((li_t & 3) >> 1) * 16 +
-                       (li_t & 1) * 8 + wave * kCols * 2;
+      const int voff = wide_voff(ln, wave * kCols);
 #pragma unroll
       for (int c0 = 0; c0 < kCB; c0 += kCBC) {
         bf16x8 vf[kCBC];
@@ -1237,25 +1460,24 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
           const int cb = c0 + c;
           if constexpr (kTrV) {
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(tile + voff + cb * 32));
+                (__attribute__((address_space(3))) i16x4*)(tile + voff + cb * 1024));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(tile + voff + 16 * kPipeRow + cb * 32));
+                (__attribute__((address_space(3))) i16x4*)(tile + voff + 256 + cb * 1024));
             vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           } else {
-            const int col = wave * kCols + cb * 16 + li;
-            const uint8_t* p0 = tile + 4 * grp * kPipeRow + (col >> 3) * 16 + (col & 7) * 2;
+            const int x = (wave * kCols + cb * 16 + li) * 2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              vf[c][i] = *reinterpret_cast<const __bf16*>(p0 + i * kPipeRow);
-              vf[c][4 + i] = *reinterpret_cast<const __bf16*>(p0 + (16 + i) * kPipeRow);
+              vf[c][i] = *reinterpret_cast<const __bf16*>(tile + wide_off(4 * grp + i, x));
+              vf[c][4 + i] = *reinterpret_cast<const __bf16*>(tile + wide_off(16 + 4 * grp + i, x));
             }
           }
         }
-        bf16x8 pf = __builtin_bit_cast(bf16x8, sh.p[grp_t][li_t]);
+        bf16x8 pf = __builtin_bit_cast(bf16x8, sh.p[0][grp_t][li_t]);
 #pragma unroll
         for (int hg = 0; hg < kHG; ++hg) {
           bf16x8 pn = pf;
-          if (hg + 1 < kHG) pn = __builtin_bit_cast(bf16x8, sh.p[grp_t][(hg + 1) * 16 + li_t]);
+          if (hg + 1 < kHG) pn = __builtin_bit_cast(bf16x8, sh.p[0][grp_t][(hg + 1) * 16 + li_t]);
 #pragma unroll
           for (int c = 0; c < kCBC; ++c)
             o[c0 + c][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c], pf, o[c0 + c][hg], 0, 0, 0);
@@ -1416,6 +1638,10 @@ mla_combine_kernel(MlaArgs a) {
 // Value fragments are read with the LDS transpose instruction unless
 // DS32CP_MLA_SCALAR_V=1 selects the element-wise reads (same results; used
 // to cross-check the transpose layout).
+static bool mla_lag() {
+  const char* e = getenv("DS32CP_MLA_LAG");
+  return !(e && e[0] == '0');
+}
 static bool mla_transpose_reads() {
   const char* e = getenv("DS32CP_MLA_SCALAR_V");
   return !(e && e[0] == '1');
@@ -1502,16 +1728,21 @@ ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
     }
     else switch (a.n_heads) {
       case 32:
-        if (tr) mla_bf16_wide_kernel<true, 1><<<blocks, kWave * 1, 0, s>>>(a, per_split);
-        else mla_bf16_wide_kernel<false, 1><<<blocks, kWave * 1, 0, s>>>(a, per_split);
+        if (tr) mla_bf16_wide_kernel<true, 1, false><<<blocks, kWave * 1, 0, s>>>(a, per_split);
+        else mla_bf16_wide_kernel<false, 1, false><<<blocks, kWave * 1, 0, s>>>(a, per_split);
         break;
       case 64:
-        if (tr) mla_bf16_wide_kernel<true, 2><<<blocks, kWave * 2, 0, s>>>(a, per_split);
-        else mla_bf16_wide_kernel<false, 2><<<blocks, kWave * 2, 0, s>>>(a, per_split);
+        if (tr) mla_bf16_wide_kernel<true, 2, false><<<blocks, kWave * 2, 0, s>>>(a, per_split);
+        else mla_bf16_wide_kernel<false, 2, false><<<blocks, kWave * 2, 0, s>>>(a, per_split);
         break;
       default:
-        if (tr) mla_bf16_wide_kernel<true, 4><<<blocks, kWave * 4, 0, s>>>(a, per_split);
-        else mla_bf16_wide_kernel<false, 4><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+        if (mla_lag()) {
+          if (tr) mla_bf16_wide_kernel<true, 4, true><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+          else mla_bf16_wide_kernel<false, 4, true><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+        } else {
+          if (tr) mla_bf16_wide_kernel<true, 4, false><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+          else mla_bf16_wide_kernel<false, 4, false><<<blocks, kWave * 4, 0, s>>>(a, per_split);
+        }
     }
     ds_status st = check_launch("sparse_mla");
     if (st != DS_OK || a.n_splits == 1) return st;
