@@ -875,6 +875,20 @@ mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
   }
 }
 
+// Maxima as the bare instructions: the inputs are finite or -inf, and the
+// library's fmaxf would first quiet possible signalling NaNs (one more
+// instruction per operand that is not known to be canonical).
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float d;
+  asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order:
 // a loop whose index is a constant expression in the body.
 template <class F, int... U>
@@ -975,7 +989,7 @@ template <int kNW>
 struct MlaWideShared {
   static constexpr int kHeads = 32 * kNW;
   uint4 qrope[2][4][kHeads];   // rope k-steps of Q^T: [ks-16][lane group][head]
-  int32_t sidx[kMlaMaxKeys];
+  int32_t sidx[kMlaMaxKeys + kPipeTile];   // + one tile of -1: the lagged loop's last gather
   uint4 p[2][4][kHeads];       // P^T fragments: [tile parity][lane group][head] -> 8 bf16
   int32_t wave_cnt[kNW];       // index compaction scratch
   int32_t bail[kNW];           // wave w saw a tile beyond its reference + 2^kWideBail
@@ -1038,7 +1052,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
     __syncthreads();
   }
   const int32_t n_tiles = static_cast<int32_t>(ceil_div(n_valid, kPipeTile));
-  for (int32_t i = n_valid + tid; i < n_tiles * kPipeTile; i += kThreads) sh.sidx[i] = -1;
+  for (int32_t i = n_valid + tid; i < (n_tiles + 1) * kPipeTile; i += kThreads) sh.sidx[i] = -1;
   if (tid < kNW) sh.bail[tid] = 0;
 
   // Q^T fragments (B operand of QK) of heads h0 and h0+16: dims 32*ks +
@@ -1223,22 +1237,22 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
     auto micro = [&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
       if constexpr (u < 2) {                       // raw maximum of head block u
-        float m = fmaxf(fmaxf(st[0][u][0], st[0][u][1]), fmaxf(st[0][u][2], st[0][u][3]));
-        m = fmaxf(m, fmaxf(fmaxf(st[1][u][0], st[1][u][1]), fmaxf(st[1][u][2], st[1][u][3])));
-        mx[u] = m;
+        const float m0 = max3_raw(st[0][u][0], st[0][u][1], st[0][u][2]);
+        const float m1 = max3_raw(st[0][u][3], st[1][u][0], st[1][u][1]);
+        mx[u] = max3_raw(m0, m1, max_raw(st[1][u][2], st[1][u][3]));
       } else if constexpr (u == 2) {               // across the four 16-lane rows
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const auto a2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[hb]),
                                                             __float_as_uint(mx[hb]), false, false);
-          mx[hb] = fmaxf(__uint_as_float(a2[0]), __uint_as_float(a2[1]));
+          mx[hb] = max_raw(__uint_as_float(a2[0]), __uint_as_float(a2[1]));
         }
       } else if constexpr (u == 3) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const auto b2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx[hb]),
                                                             __float_as_uint(mx[hb]), false, false);
-          mx[hb] = fmaxf(__uint_as_float(b2[0]), __uint_as_float(b2[1])) * scale2;
+          mx[hb] = max_raw(__uint_as_float(b2[0]), __uint_as_float(b2[1])) * scale2;
         }
       } else if constexpr (u == 4) {
 #pragma unroll
@@ -1336,7 +1350,10 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       // QK of tile t (buffer b) with the gather of tile t+1 spread through it
       auto qk_tile = [&](int32_t t, int b, f32x4 (&st)[2][2]) __attribute__((always_inline)) {
         const uint8_t* tile = g_mla_bufs + b * kPipeTileBytes;
-        qk(tile, st, t + 1 < n_tiles, (t + 1) * kPipeTile, b == 2 ? 0 : b + 1);
+        // the gather of tile t+1 is issued unconditionally (after the last
+        // tile it reads padding rows into a free buffer), so the k-step loop
+        // has no branch; the epilogue waits for it before reusing the buffers
+        qk(tile, st, true, (t + 1) * kPipeTile, b == 2 ? 0 : b + 1);
         // valid rows are compacted to the front: only the last tile is
         // partial; its missing keys get a logit of -inf (weight 0)
         const int32_t rem = n_valid - t * kPipeTile;
@@ -1504,6 +1521,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       sh.l_fin[h0 + 16 * hb] = l_run[hb];
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);   // the lagged loop's last gather (into a tile buffer)
   __syncthreads();   // also: every wave is done with the tile buffers
   const int col0 = wave * kCols + grp * 4;
   auto write_out = [&](auto esz) {
