@@ -89,6 +89,16 @@ indexer_f32_kernel(IndexerArgs a) {
   a.scores[static_cast<int64_t>(j) * a.score_stride + p] = score;
 }
 
+// ReLU as one integer max of the bit pattern: a float with the sign bit set
+// (negative, or -0) is a negative int and becomes +0, any other is kept.
+// Exact for every non-NaN input (the MFMA results are finite); fmaxf would
+// first quiet a possible signalling NaN with one more instruction per
+// element, a third of the head-sum epilogue.
+__device__ __forceinline__ float relu_raw(float x) {
+  const int32_t b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
+
 // ------------------------------------------------------- MFMA constants
 constexpr int kIxHeads = 64;
 constexpr int kIxDim = 128;
@@ -118,7 +128,7 @@ __device__ __forceinline__ float head_sum(const f32x16 (&acc)[kIxRowBlocks],
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int h = rb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      v = fmaf(w_heads[h], fmaxf(acc[rb][i], 0.f), v);
+      v = fmaf(w_heads[h], relu_raw(acc[rb][i]), v);
     }
   }
   v += __shfl_xor(v, 32);
@@ -366,7 +376,7 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
 #pragma unroll
         for (int rb = 0; rb < kIxRowBlocks; ++rb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], fmaxf(acc[nb][rb][i], 0.f), v);
+          for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], relu_raw(acc[nb][rb][i]), v);
         // the other half of the heads sits in lanes l^32
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
                                                          false, false);
@@ -581,7 +591,7 @@ indexer_paged_mfma_kernel(IndexerArgs a) {
 #pragma unroll
       for (int rb = 0; rb < kIxRowBlocks; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v = fmaf(wr[rb][i], fmaxf(acc[rb][i], 0.f), v);
+        for (int i = 0; i < 16; ++i) v = fmaf(wr[rb][i], relu_raw(acc[rb][i]), v);
       v += __shfl_xor(v, 32);
       const int64_t p = kIxDUnit * s + lane;
       if (lane < 32 && p < L) {
