@@ -197,6 +197,26 @@ def test_rerange_host_built_concat_all_row_sizes(row_shape, dtype):
         assert np.array_equal(gp.raw_bytes(got).reshape(T, rb), orr.rerange(cat, T, cp, slot))
 
 
+def test_mla_rejects_scale_that_is_not_positive_and_finite():
+    # the softmax maximum is taken on raw dot products and scaled afterwards,
+    # which needs sm_scale > 0; the host check returns DS_ERR_INVALID_ARG
+    # before any launch, and the output is left untouched
+    q = torch.zeros(2, 128, 576, device=gp.DEV, dtype=torch.bfloat16)
+    kv = torch.zeros(40, 576, device=gp.DEV, dtype=torch.bfloat16)
+    idx = torch.arange(64, device=gp.DEV, dtype=torch.int32).view(2, 32) % 40
+    for fn in (ds.sparse_mla_prefill, ds.sparse_mla_decode):
+        for sc in (0.0, -0.5, float("inf"), float("nan")):
+            out = torch.full((2, 128, 512), 7.0, device=gp.DEV, dtype=torch.bfloat16)
+            with pytest.raises(ds.DS32CPError) as ei:
+                fn(q, kv, idx, sc, 512, out=out)
+            assert ei.value.status == 1, ei.value   # DS_ERR_INVALID_ARG
+            torch.cuda.synchronize()
+            assert bool((out == 7.0).all())
+    o, _ = ds.sparse_mla_prefill(q, kv, idx, 1e-3, 512)   # a valid scale still runs
+    torch.cuda.synchronize()
+    assert bool((o == 0).all())
+
+
 def test_mla_empty_and_out_of_range_rows():
     wl = get("tiny_prefill_bf16")
     rng = np.random.default_rng(5)
