@@ -1030,16 +1030,48 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   int32_t s_end = s_begin + keys_per_split;
   s_end = s_end < a.topk ? s_end : a.topk;
   const int32_t n_keys = s_end > s_begin ? s_end - s_begin : 0;
-  // valid row indices, compacted in their given order (ordered ballot scan)
+  // Loads first, all in flight together: the selected row indices (every
+  // one of the split's, kIdx per thread) and Q^T.  The compaction below
+  // then waits only for the indices, and Q lands while it runs.
   const int32_t* idx_row = a.topk_idx + static_cast<int64_t>(j) * a.topk + s_begin;
+  constexpr int kIdx = kMlaMaxKeys / kThreads;
+  int32_t ridx[kIdx];
+#pragma unroll
+  for (int it = 0; it < kIdx; ++it) {
+    const int32_t i = it * kThreads + tid;
+    ridx[it] = i < n_keys ? idx_row[i] : -1;
+  }
+  // Q^T fragments (B operand of QK) of heads h0 and h0+16: dims 32*ks +
+  // 8*grp + 0..7; the latent k-steps in VGPRs, the 2 rope k-steps in LDS
+  bf16x8 qf[2][kQReg];
+  auto q_of = [&](int hb) {
+    return static_cast<const uint16_t*>(a.q) +
+           (static_cast<int64_t>(j) * a.n_heads + h0 + 16 * hb) * kMlaD + grp * 8;
+  };
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const uint16_t* q = q_of(hb);
+#pragma unroll
+    for (int ks = 0; ks < kQReg; ++ks)
+      qf[hb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
+  }
+  // valid row indices, compacted in their given order (ordered ballot
+  // scan); LDS-only barriers, so the Q loads stay in flight
+  auto lds_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   int32_t n_valid = 0;
-  for (int32_t i0 = 0; i0 < n_keys; i0 += kThreads) {
-    const int32_t i = i0 + tid;
-    const int32_t r = i < n_keys ? idx_row[i] : -1;
+#pragma unroll
+  for (int it = 0; it < kIdx; ++it) {
+    if (it * kThreads >= n_keys) continue;   // uniform
+    const int32_t r = ridx[it];
     const bool ok = r >= 0 && r < a.kv_rows;
     const uint64_t ball = __ballot(ok);
     if (lane == 0) sh.wave_cnt[wave] = static_cast<int32_t>(__popcll(ball));
-    __syncthreads();
+    lds_barrier();
     int32_t before = n_valid, total = 0;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
@@ -1049,26 +1081,11 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
     }
     if (ok) sh.sidx[before + __popcll(ball & ((1ull << lane) - 1ull))] = r;
     n_valid += total;
-    __syncthreads();
+    lds_barrier();
   }
   const int32_t n_tiles = static_cast<int32_t>(ceil_div(n_valid, kPipeTile));
   for (int32_t i = n_valid + tid; i < (n_tiles + 1) * kPipeTile; i += kThreads) sh.sidx[i] = -1;
   if (tid < kNW) sh.bail[tid] = 0;
-
-  // Q^T fragments (B operand of QK) of heads h0 and h0+16: dims 32*ks +
-  // 8*grp + 0..7; the latent k-steps in VGPRs, the 2 rope k-steps in LDS
-  bf16x8 qf[2][kQReg];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        (static_cast<int64_t>(j) * a.n_heads + h0 + 16 * hb) * kMlaD + grp * 8;
-#pragma unroll
-    for (int ks = 0; ks < kQReg; ++ks)
-      qf[hb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      sh.qrope[r][grp][h0 + 16 * hb] = *reinterpret_cast<const uint4*>(q + (kQReg + r) * 32);
-  }
   const float scale2 = a.sm_scale * kLog2e;
   const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
   const uint32_t lds_bufs = static_cast<uint32_t>(
@@ -1089,8 +1106,18 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) wide_gather_issue(kv, slot_lds(b, i), slot_off(base, i));
   };
-  // Q loads complete before any gather is in flight (a wait for them inside
-  // the tile loop would also wait for the gathers)
+  // The first tile's gather goes out before the rope part of Q is loaded,
+  // so that the two latencies overlap (the lagged loop issues it here on its
+  // first pass; the padding rows of the index list must be visible first).
+  // Then everything lands before the tile loop: the compiler's own waits for
+  // Q inside the loop would not account for the gathers.
+  lds_barrier();
+  if (kLag && n_tiles > 0) issue_tile(0, 0);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      sh.qrope[r][grp][h0 + 16 * hb] = *reinterpret_cast<const uint4*>(q_of(hb) + (kQReg + r) * 32);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
@@ -1337,7 +1364,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
 #pragma unroll
       for (int hg = 0; hg < kHG; ++hg) o[cb][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_run[0] = l_run[1] = 0.f;
-    if (n_tiles > 0) issue_tile(0, 0);
+    if (n_tiles > 0 && (exact || !kLag)) issue_tile(0, 0);
     if (!kLag && n_tiles > 1) issue_tile(1, kPipeTile);
     bool bailed = false;
     if constexpr (kLag) {
