@@ -36,12 +36,11 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round-to-nearest-even float -> bfloat16 bits (NaN kept quiet).
+// Round-to-nearest-even float -> bfloat16 bits (NaN stays NaN): gfx950's
+// conversion instruction (v_cvt_pk_bf16_f32, two values per instruction
+// when the compiler pairs them) instead of the integer rounding sequence.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet = (u >> 16) | 0x40u;
-  return static_cast<uint16_t>(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Two OCP e4m3fn codes (bytes 0,1 of `word`, or bytes 2,3 when kHi) ->

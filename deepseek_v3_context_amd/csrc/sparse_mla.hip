@@ -1592,6 +1592,8 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       constexpr int kPieces = kRowB / 16;   // 16-byte pieces per head row
+      // unrolled: all of a thread's LDS reads are issued before its stores
+#pragma unroll
       for (int i = tid; i < kCH * kPieces; i += kThreads) {
         const int r = i / kPieces, q = i - r * kPieces;
         const int h = c * kCH + r;
