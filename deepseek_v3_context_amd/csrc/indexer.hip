@@ -237,12 +237,19 @@ __device__ __forceinline__ bf16x8 ix_bfrag(const uint8_t* tile, int nb, int ks, 
   }
 }
 
-constexpr int32_t kIxPChunkKeys = 2048;   // key rows per workgroup
+// Key rows per workgroup: 21 bf16 tiles or 10 fp8 tiles, the most whose
+// scores still fit in LDS beside the two tile buffers.  Longer chunks mean
+// fewer workgroups per query block: on causal prefills of a few thousand
+// queries the grid then fits on the CUs in one round.
+template <bool kFp8>
+constexpr int32_t ix_chunk_keys() { return kFp8 ? 2560 : 2688; }
 
 template <bool kFp8>
 __global__ void __launch_bounds__(kWave * kIxPWaves)
 indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks) {
-  constexpr int32_t chunk_keys = kIxPChunkKeys;
+  constexpr int32_t chunk_keys = ix_chunk_keys<kFp8>();
+  static_assert(chunk_keys % IxTile<kFp8>::kTile == 0 && chunk_keys % kFp8BlockRows == 0,
+                "chunks hold whole tiles and whole fp8 scale blocks");
   __shared__ int64_t q_lo[kIxPWaves], q_hi[kIxPWaves];
   // scores of the chunk stay in LDS until the end: a global store inside
   // the tile loop would make every wait for the next tile's gather
@@ -338,7 +345,9 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
 #pragma unroll
     for (int hf = 0; hf < kTile / kIxPHalf; ++hf) {
       const int64_t hbase = base + hf * kIxPHalf;
-      if (!live || hbase >= my_hi || hbase + kIxPHalf <= my_lo) continue;
+      // (a tile can reach past the chunk when the block's range starts
+      // past the chunk's first 64 rows: those rows belong to the next chunk)
+      if (!live || hbase >= my_hi || hbase + kIxPHalf <= my_lo || hbase >= c_hi) continue;
       const uint8_t* tile = ix_buf<B>() + hf * kIxPHalf * IxTile<kFp8>::kLdsRow;
       // both 32-key column blocks at once: four independent accumulator
       // chains per wave keep the MFMA pipe busy
@@ -382,7 +391,7 @@ indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chu
                                                          false, false);
         v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const int64_t row = hbase + nb * 32 + (lane & 31);
-        if (lane < 32 && row >= my_lo && row < my_hi) sc[wave][row - c_lo] = v;
+        if (lane < 32 && row >= my_lo && row < my_hi && row < c_hi) sc[wave][row - c_lo] = v;
       }
     }
   };
@@ -664,7 +673,8 @@ ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
     return check_launch("indexer_scores (paged)");
   }
   const int32_t n_qblocks = static_cast<int32_t>(ceil_div(a.n_q, kIxPWaves));
-  const int32_t n_chunks = static_cast<int32_t>(ceil_div(a.k_rows, kIxPChunkKeys));
+  const int32_t n_chunks =
+      static_cast<int32_t>(ceil_div(a.k_rows, fp8 ? ix_chunk_keys<true>() : ix_chunk_keys<false>()));
   const uint32_t grid = static_cast<uint32_t>(round_up(static_cast<int64_t>(n_qblocks) * n_chunks, 8));
   if (fp8)
     indexer_prefill_pipelined_kernel<true><<<grid, kWave * kIxPWaves, 0, s>>>(
