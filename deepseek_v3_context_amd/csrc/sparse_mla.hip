@@ -1015,9 +1015,11 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
 
   // Queries in reverse order: in causal prefill the later queries select
   // the most rows, so the longest workgroups start first and the short ones
-  // fill the tail.
-  const int32_t jr = blockIdx.x / a.n_splits;
-  const int32_t split = blockIdx.x - jr * a.n_splits;
+  // fill the tail.  Split-major ids (decode): the splits of a query are
+  // n_q ids apart, so with n_q a multiple of 8 they run on one XCD, whose L2
+  // then serves the query's Q to all of them.
+  const int32_t jr = blockIdx.x % a.n_q;
+  const int32_t split = blockIdx.x / a.n_q;
   const int32_t j = a.n_q - 1 - jr;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
