@@ -78,7 +78,7 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   constexpr int kTkWaves = kTkThreads / kWave;
   extern __shared__ __align__(16) uint32_t cache[];
   __shared__ uint32_t hist[kTkWaves][256];   // one histogram per wave (less contention)
-  __shared__ uint32_t sh_digit, sh_remaining;
+  __shared__ uint32_t sh_digit, sh_remaining, sh_count, sh_ncand;
   __shared__ uint32_t wave_tot[kTkWaves];
   __shared__ int32_t sel_t[kTopkMax];        // selected elements in output order (kMode 0, 2)
 
@@ -188,32 +188,46 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   if (cached) load_block(0);
 
   uint32_t prefix = 0, mask = 0, remaining = static_cast<uint32_t>(a.topk);
+  // Histogram of digit `shift` of the keys that match the prefix so far,
+  // over keys 0..n-1 of the staged block.
+  auto count_keys = [&](int32_t n, int shift) {
+    for (int32_t t0 = tid * kTkPer; t0 < n; t0 += kTkThreads * kTkPer) {
+      uint32_t u[kTkPer];
+      read_keys(t0, n, u);
+#pragma unroll
+      for (int k = 0; k < kTkPer; ++k) {
+        const bool in = t0 + k < n && (u[k] & mask) == prefix;
+        const uint32_t d = (u[k] >> shift) & 255u;
+        // Scores of a row often share their top bits: lanes of the wave
+        // with the digit of the first active lane are counted with one add.
+        const uint64_t act = __ballot(in);
+        if (act == 0ull) continue;
+        const int first = static_cast<int>(__builtin_ctzll(act));
+        const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
+        const uint64_t same = __ballot(in && d == d0);
+        if (lane == first) atomicAdd(&hist[wave][d0], static_cast<uint32_t>(__popcll(same)));
+        if (in && d != d0) atomicAdd(&hist[wave][d], 1u);
+      }
+    }
+  };
+  // Rows longer than the cache: after the first pass only the keys in the
+  // threshold's top-byte bucket matter to the next three, so when they fit
+  // they are compacted into the cache once (one more read of the row) and
+  // the later passes count them there instead of reading the row again.
+  bool cand = false;
+  int32_t n_cand = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < kTkWaves * 256; i += kTkThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int32_t b0 = 0; b0 < L; b0 += cache_keys) {
-      if (!cached) {
-        __syncthreads();   // the previous block is fully counted
-        load_block(b0);
-      }
-      const int32_t n = block_len(b0);
-      for (int32_t t0 = tid * kTkPer; t0 < n; t0 += kTkThreads * kTkPer) {
-        uint32_t u[kTkPer];
-        read_keys(t0, n, u);
-#pragma unroll
-        for (int k = 0; k < kTkPer; ++k) {
-          const bool in = t0 + k < n && (u[k] & mask) == prefix;
-          const uint32_t d = (u[k] >> shift) & 255u;
-          // Scores of a row often share their top bits: lanes of the wave
-          // with the digit of the first active lane are counted with one add.
-          const uint64_t act = __ballot(in);
-          if (act == 0ull) continue;
-          const int first = static_cast<int>(__builtin_ctzll(act));
-          const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
-          const uint64_t same = __ballot(in && d == d0);
-          if (lane == first) atomicAdd(&hist[wave][d0], static_cast<uint32_t>(__popcll(same)));
-          if (in && d != d0) atomicAdd(&hist[wave][d], 1u);
+    if (cand) {
+      count_keys(n_cand, shift);
+    } else {
+      for (int32_t b0 = 0; b0 < L; b0 += cache_keys) {
+        if (!cached) {
+          __syncthreads();   // the previous block is fully counted
+          load_block(b0);
         }
+        count_keys(block_len(b0), shift);
       }
     }
     __syncthreads();
@@ -240,6 +254,7 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
         if (cum < remaining && cum + c[b] >= remaining) {
           sh_digit = 4u * lane + b;
           sh_remaining = remaining - cum;
+          sh_count = c[b];
         }
         cum += c[b];
       }
@@ -249,6 +264,38 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
     mask |= 255u << shift;
     remaining = sh_remaining;
     __syncthreads();
+    if (kMode == 0 && shift == 24 && !cached && sh_count <= static_cast<uint32_t>(cache_keys)) {
+      // uniform: every thread read the same sh_count
+      if (tid == 0) sh_ncand = 0;
+      __syncthreads();   // (the cache's last staged block is fully counted)
+      constexpr int kU = 16;
+      for (int32_t r0 = 0; r0 < L; r0 += kU * kTkThreads) {
+        float v[kU];
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+          const int32_t t = r0 + k * kTkThreads + tid;
+          v[k] = t < L ? row_scores[t] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+          const int32_t t = r0 + k * kTkThreads + tid;
+          const uint32_t u = float_order_key(v[k]);
+          const bool m = t < L && (u & mask) == prefix;
+          const uint64_t bm = __ballot(m);
+          if (bm == 0ull) continue;
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(&sh_ncand, static_cast<uint32_t>(__popcll(bm)));
+          base = __shfl(base, 0);
+          const uint32_t slot = base + static_cast<uint32_t>(__popcll(bm & ((1ull << lane) - 1ull)));
+          if (m && slot < static_cast<uint32_t>(cache_keys)) cache[slot] = u;
+        }
+      }
+      __syncthreads();
+      n_cand = static_cast<int32_t>(sh_ncand < static_cast<uint32_t>(cache_keys) ? sh_ncand
+                                                                           : static_cast<uint32_t>(cache_keys));
+      cand = true;
+      __syncthreads();   // sh_ncand read by all before any later write
+    }
   }
 
   // prefix is now the k-th largest key; `remaining` copies of it are taken.
