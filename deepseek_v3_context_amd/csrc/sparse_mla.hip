@@ -1631,54 +1631,63 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   }
 }
 
-// Merge split partials: one workgroup per (query, head), one thread per
-// output column pair.
+// Merge split partials: one workgroup per (query, 4 heads), 64 threads per
+// head, 8 output columns (one 16-byte load per split) per thread.
 constexpr int kMlaMaxSplits = 16;   // topk <= 2048 rows, at least 4 tiles per split
+constexpr int kMlaCombineHeads = 4;
 
 __global__ void __launch_bounds__(256)
 mla_combine_kernel(MlaArgs a) {
   const int32_t j = blockIdx.x;
-  const int32_t h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int c = tid * 2;
-  // every split's (m, l) and this thread's two columns, all loads in flight
+  const int32_t h = blockIdx.y * kMlaCombineHeads + (tid >> 6);
+  const int c = (tid & 63) * 8;
+  // every split's (m, l) and this thread's eight columns, all loads in flight
   float ms[kMlaMaxSplits], ls[kMlaMaxSplits];
-  uint32_t v[kMlaMaxSplits];
+  uint4 v[kMlaMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMlaMaxSplits; ++s) {
     if (s < a.n_splits) {
       const float* pml = mla_partial_ml(a, j, s, h);
       ms[s] = pml[0];
       ls[s] = pml[1];
-      v[s] = *reinterpret_cast<const uint32_t*>(mla_partial_o(a, j, s, h) + c);
+      v[s] = *reinterpret_cast<const uint4*>(mla_partial_o(a, j, s, h) + c);
     } else {
       ms[s] = -INFINITY;
       ls[s] = 0.f;
-      v[s] = 0u;
+      v[s] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kMlaMaxSplits; ++s) M = fmaxf(M, ms[s]);
-  float Lsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+  float Lsum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMlaMaxSplits; ++s) {
     const float wgt = ms[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[s] - M);
     Lsum += ls[s] * wgt;
-    acc0 = fmaf(bf16_bits_to_f32(static_cast<uint16_t>(v[s] & 0xffffu)), wgt, acc0);
-    acc1 = fmaf(bf16_bits_to_f32(static_cast<uint16_t>(v[s] >> 16)), wgt, acc1);
+    const uint32_t w4[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[2 * k] = fmaf(bf16_bits_to_f32(static_cast<uint16_t>(w4[k] & 0xffffu)), wgt, acc[2 * k]);
+      acc[2 * k + 1] = fmaf(bf16_bits_to_f32(static_cast<uint16_t>(w4[k] >> 16)), wgt, acc[2 * k + 1]);
+    }
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + c;
   if (a.out_dtype == DS_BF16) {
-    uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
-    *reinterpret_cast<uint32_t*>(out) =
-        f32_to_bf16_bits(acc0 * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc1 * inv)) << 16);
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = f32_to_bf16_bits(acc[2 * k] * inv) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * k + 1] * inv)) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + obase) = make_uint4(o[0], o[1], o[2], o[3]);
   } else {
     float* out = static_cast<float*>(a.out) + obase;
-    *reinterpret_cast<float2*>(out) = make_float2(acc0 * inv, acc1 * inv);
+    *reinterpret_cast<float4*>(out) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   }
-  if (a.lse && tid == 0)
+  if (a.lse && (tid & 63) == 0)
     a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
         Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
@@ -1795,8 +1804,8 @@ ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
     }
     ds_status st = check_launch("sparse_mla");
     if (st != DS_OK || a.n_splits == 1) return st;
-    dim3 cgrid(a.n_q, a.n_heads);
-    mla_combine_kernel<<<cgrid, kMlaDl / 2, 0, s>>>(a);
+    dim3 cgrid(a.n_q, a.n_heads / kMlaCombineHeads);
+    mla_combine_kernel<<<cgrid, 256, 0, s>>>(a);
     return check_launch("sparse_mla combine");
   }
   const int threads = kWave * (a.n_heads / (16 * kMlaGroups));
@@ -1809,8 +1818,8 @@ ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
   }
   ds_status st = check_launch("sparse_mla");
   if (st != DS_OK || a.n_splits == 1) return st;
-  dim3 cgrid(a.n_q, a.n_heads);
-  mla_combine_kernel<<<cgrid, kMlaDl / 2, 0, s>>>(a);
+  dim3 cgrid(a.n_q, a.n_heads / kMlaCombineHeads);
+  mla_combine_kernel<<<cgrid, 256, 0, s>>>(a);
   return check_launch("sparse_mla combine");
 }
 
