@@ -24,6 +24,7 @@ import torch
 
 from oracle import pipeline as opl
 from oracle import round_robin_cp as orr
+from oracle import sparse_attention as sa
 from synth import draw_decode, draw_prefill, get
 
 pytestmark = pytest.mark.gpu
@@ -341,3 +342,79 @@ def test_integer_outputs_repeatable():
     b = gp.run_prefill(wl, inp, want_scores=False)
     assert np.array_equal(a["topk_idx"], b["topk_idx"])
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
+
+
+@pytest.mark.parametrize("heads", [32, 64])
+def test_mla_head_counts_below_128(heads):
+    # the ABI takes any head count that is a multiple of 32 (up to 128): the
+    # kernels for 32 and 64 heads (one or two waves per query), prefill and
+    # decode (split partials merged by the combine), against the oracle
+    rng = np.random.default_rng(40 + heads)
+    g = torch.Generator(device="cpu").manual_seed(40 + heads)
+    n, rows, k = 20, 2000, 256
+    q = (torch.randn(n, heads, 576, generator=g) / 24).bfloat16().to(gp.DEV)
+    kv = (torch.randn(rows, 576, generator=g) / 24).bfloat16().to(gp.DEV)
+    idx = np.full((n, k), -1, dtype=np.int32)
+    for j in range(n):
+        cnt = int(rng.integers(1, k + 1)) if j % 3 else k   # ragged tails
+        idx[j, :cnt] = rng.choice(rows, cnt, replace=False)
+    idx_t = torch.from_numpy(idx).to(gp.DEV)
+    scale = 1.0 / 24.0
+    qb, kvb = q.view(torch.int16).cpu().numpy(), kv.view(torch.int16).cpu().numpy()
+    ref_o, ref_l = opl.sparse_mla_rows(list(range(n)), list(idx), qb, "bf16", kvb, "bf16", None,
+                                       scale, 512)
+    for fn in (ds.sparse_mla_prefill, ds.sparse_mla_decode):
+        o, lse = fn(q, kv, idx_t, scale, 512)
+        torch.cuda.synchronize()
+        err = np.abs(o.float().cpu().numpy() - ref_o).max()
+        rel = err / np.abs(ref_o).max()
+        lerr = np.abs(lse.cpu().numpy() - ref_l).max()
+        gp.say(f"  {heads} heads {fn.__name__}: max|dO|={err:.3e} rel={rel:.3e} max|dlse|={lerr:.3e}")
+        assert err <= 2e-2 and rel <= 1e-2, (fn.__name__, err, rel)
+        assert lerr <= 1e-3, (fn.__name__, lerr)
+    # decode with few queries and more rows per query: four splits each
+    q4 = q[:4].contiguous()
+    idx4 = np.full((4, 1024), -1, dtype=np.int32)
+    for j in range(4):
+        idx4[j, : 1024 - 100 * j] = rng.choice(rows, 1024 - 100 * j, replace=False)
+    o4, l4 = ds.sparse_mla_decode(q4, kv, torch.from_numpy(idx4).to(gp.DEV), scale, 512)
+    torch.cuda.synchronize()
+    r4o, r4l = opl.sparse_mla_rows(list(range(4)), list(idx4), qb, "bf16", kvb, "bf16", None,
+                                   scale, 512)
+    err = np.abs(o4.float().cpu().numpy() - r4o).max()
+    assert err <= 2e-2 and err / np.abs(r4o).max() <= 1e-2, err
+    assert np.abs(l4.cpu().numpy() - r4l).max() <= 1e-3
+
+
+def test_topk_rows_longer_than_the_cache():
+    # rows longer than the 32768-key LDS cache: the threshold bucket is
+    # compacted into the cache after the first radix pass when it fits, and
+    # the row is re-read per pass when it does not; ties go to the lower
+    # position.  The decision is on the same float32 values, so the selected
+    # sets must equal the oracle's exactly.
+    rng = np.random.default_rng(51)
+    L, k = 40000, 2048
+    rows = []
+    rows.append(rng.standard_normal(L).astype(np.float32))                 # compacted bucket
+    rows.append(np.full(L, 0.5, dtype=np.float32))                         # bucket > cache: all tied
+    rows.append(rng.choice(np.array([-1.0, 0.25, 0.5, 2.0], dtype=np.float32), L))   # heavy ties
+    r3 = (1.0 + rng.random(L)).astype(np.float32)                          # 38000 in [1, 2) ...
+    r3[rng.choice(L, 2000, replace=False)] = 4.0                           # ... 2000 above: bucket > cache
+    rows.append(r3)
+    rows.append(rng.standard_normal(L).astype(np.float32))                 # short row (select all)
+    lens = np.array([L, L, L, 36000, 1000], dtype=np.int32)
+    scores = np.full((len(rows), L), np.nan, dtype=np.float32)
+    for i, r in enumerate(rows):
+        scores[i, : lens[i]] = r[: lens[i]]
+    dev_scores = torch.from_numpy(scores).to(gp.DEV)
+    kv_start = torch.zeros(len(rows), dtype=torch.int32, device=gp.DEV)
+    kv_len = torch.from_numpy(lens).to(gp.DEV)
+    idx, _ = ds.topk_select(dev_scores, kv_start, kv_len, L, k, L)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for i in range(len(rows)):
+        want = np.sort(sa.topk_positions(scores[i, : lens[i]], k))
+        g_i = got[i][got[i] >= 0]
+        assert (np.diff(g_i) > 0).all(), f"row {i}: not in position order"
+        assert np.array_equal(g_i, want), f"row {i}: {np.setxor1d(g_i, want).size} differences"
+        assert (got[i][g_i.size:] == -1).all()
