@@ -10,12 +10,18 @@ already resident in HBM:
   decode:  indexer_topk (scores + top-k in one call) on the paged pool,
            sparse MLA (decode).
 
-The step is timed end to end (K steps between two device synchronisations)
-and per call with HIP events on the stream the library launches on.  The
-printed JSON carries the roofline of the dominant kernel and the CPU
-oracle's rate on a bounded sample of the same workload.
+After the W warm-up steps, untimed steps keep running for a short settle
+time (200 ms by default): a cold MI355X runs the first tens of milliseconds
+of work at a visibly lower clock.  A HIP event pair costs a few microseconds
+of device time, so events stay out of the calls that are not being
+measured: a first pass of K steps brackets every call with events (the
+per-kernel table, and which kernel dominates); the timed region then runs
+K steps with events around the dominant call only, and its wall clock
+between two device synchronisations gives the step time.  The printed JSON carries the roofline of the dominant
+kernel, taken from the timed region, and the CPU oracle's rate on a bounded
+sample of the same workload.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--settle-ms MS]
 """
 
 from __future__ import annotations
@@ -41,19 +47,27 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_t8000_cp8")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="after the warm-up steps, keep running untimed steps for at least this "
+                         "long so that the GPU clocks have ramped (0 = off)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
 
 
 class Timed:
-    """HIP-event timing of named calls on the current stream."""
+    """HIP-event timing of named calls on the current stream (of every call,
+    or of the calls named in `only`; the others run unbracketed)."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, only=None):
         self.torch = torch
+        self.only = only
         self.events = {}
 
     def run(self, name, fn):
+        if self.only is not None and name not in self.only:
+            fn()
+            return
         t = self.torch
         s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         s.record()
@@ -305,23 +319,40 @@ def main():
         step = decode_step
     torch.cuda.synchronize()
 
-    warm = Timed(torch)
+    warm = Timed(torch, only=())
     for _ in range(args.warmup):
         step(wl, ds, st, warm)
     torch.cuda.synchronize()
+    # clock settle: a cold GPU runs the first tens of milliseconds of work
+    # well below its steady clock; keep at most 8 steps queued so that the
+    # host clock tracks the device's
+    settle_steps, t_settle = 0, time.perf_counter()
+    while args.settle_ms > 0 and time.perf_counter() - t_settle < args.settle_ms * 1e-3:
+        step(wl, ds, st, warm)
+        settle_steps += 1
+        if settle_steps % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     if wl.kind == "prefill":
         kv_len_host = st["meta"]["kv_len"].cpu().numpy()
     else:
         kv_len_host = st["inp"]["lengths"]
+    print(f"[bench] per-call pass, {args.steps} steps", file=sys.stderr, flush=True)
+    calls = Timed(torch)
+    for _ in range(args.steps):
+        step(wl, ds, st, calls)
+    torch.cuda.synchronize()
+    per_call = calls.avg_ms()
+    dom = max(per_call, key=per_call.get)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    tm = Timed(torch)
+    tm = Timed(torch, only=(dom,))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(wl, ds, st, tm)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per_call = tm.avg_ms()
     model, idx_pairs, mla_pairs = work_model(wl, kv_len_host)
     kernels = {}
     for name, ms in per_call.items():
@@ -329,19 +360,18 @@ def main():
         kernels[name] = {"avg_us": round(ms * 1e3, 2),
                          "tflops": round(w["flops"] / (ms * 1e-3) / 1e12, 2),
                          "gbs": round(w["bytes"] / (ms * 1e-3) / 1e9, 1)}
-    dom = max(per_call, key=per_call.get)
     dw = model[dom]
-    d_ms = per_call[dom]
+    d_ms = tm.avg_ms()[dom]
     # prefill indexer and MLA are dense contractions over tiles (MFMA-bound);
     # decode and the permutations stream HBM
     if wl.kind == "prefill" and dom in ("sparse_mla", "indexer_scores"):
         ach = dw["flops"] / (d_ms * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+        roof = {"kernel": dom, "avg_us": round(d_ms * 1e3, 2), "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": counted_traffic(dom, wl.name)}
     else:
         ach = dw["bytes"] / (d_ms * 1e-3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
+        roof = {"kernel": dom, "avg_us": round(d_ms * 1e3, 2), "bound": "hbm", "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                 "traffic": counted_traffic(dom, wl.name)}
     n = st["n"]
@@ -360,6 +390,10 @@ def main():
                    "indexer_pairs": idx_pairs, "mla_pairs": mla_pairs},
         "roofline": roof,
         "kernels": kernels,
+        "untimed": {"warmup_steps": args.warmup, "settle_steps": settle_steps,
+                    "settle_ms": round(settle_ms, 1), "per_call_pass_steps": args.steps},
+        "kernel_timing": "kernels: separate pass, HIP events around every call; "
+                         "roofline: timed region, events around the dominant call only",
     }
     if args.cpu_seconds > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
