@@ -249,9 +249,12 @@ static ds_status check_mla(const char* fn, const MlaArgs& a) {
   } else if (a.q_dtype == DS_BF16) {
     DS_REQUIRE(a.kv_dtype == DS_BF16 || a.kv_dtype == DS_FP8_E4M3FN, DS_ERR_UNSUPPORTED,
                f + ": bf16 queries need bf16 or fp8 kv");
-    DS_REQUIRE(a.n_heads % 32 == 0 && a.n_heads <= 128 && a.d_latent == 512 && a.d_rope == 64,
+    // the kernels run 32, 64 or 128 heads per query row (a 96-head row
+    // would have them read and write a neighbouring row's heads)
+    DS_REQUIRE((a.n_heads == 32 || a.n_heads == 64 || a.n_heads == 128) && a.d_latent == 512 &&
+                   a.d_rope == 64,
                DS_ERR_UNSUPPORTED,
-               f + ": bf16 path supports n_heads % 32 == 0 (<= 128), d_latent 512, d_rope 64");
+               f + ": bf16 path supports n_heads 32, 64 or 128, d_latent 512, d_rope 64");
   } else {
     return fail(DS_ERR_UNSUPPORTED, f + ": q must be f32 or bf16");
   }

@@ -222,8 +222,8 @@ ds_status topk_select(const float* scores, int64_t score_stride,
  *   out [n_q, n_heads, d_latent] dev            out_dtype (DS_F32/DS_BF16)
  *   lse [n_q, n_heads] dev fp32, or NULL
  * Supported: all-f32 path with n_heads <= 128, d_latent + d_rope <= 640;
- * bf16 q with bf16 or fp8 kv: n_heads % 32 == 0, n_heads <= 128,
- * d_latent == 512, d_rope == 64.  topk in [1, 2048].  sm_scale must be
+ * bf16 q with bf16 or fp8 kv: n_heads 32, 64 or 128 (DS_ERR_UNSUPPORTED
+ * otherwise), d_latent == 512, d_rope == 64.  topk in [1, 2048].  sm_scale must be
  * positive and finite (DS_ERR_INVALID_ARG otherwise).
  * fp8 kv (prefill): the rows are first widened once per call into the
  * caller's workspace as bf16 values code * scale (round to nearest even;

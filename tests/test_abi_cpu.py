@@ -99,6 +99,10 @@ def test_mla_rejects_unsupported_dims_and_workspace():
     base = lambda q_dt, kv_dt, H, dl, dr, out_dt: (  # noqa: E731
         _p(), q_dt, _p(), kv_dt, None, 100, _p(), 4, H, dl, dr, 64, 0.1, _p(), out_dt, None)
     assert lib.sparse_mla_prefill(*base(1, 1, 48, 512, 64, 1), None, 0, None) == 2   # heads % 32
+    # 96 heads: the kernels run 32, 64 or 128 heads per query row
+    assert lib.sparse_mla_prefill(*base(1, 1, 96, 512, 64, 1), None, 0, None) == 2
+    need96 = ds.sparse_mla_workspace_size(4, 96, 512, 64)
+    assert lib.sparse_mla_decode(*base(1, 1, 96, 512, 64, 1), _p(), need96, None) == 2
     assert lib.sparse_mla_prefill(*base(1, 1, 128, 256, 64, 1), None, 0, None) == 2  # latent dims
     assert lib.sparse_mla_prefill(*base(0, 1, 16, 64, 16, 0), None, 0, None) == 2    # f32 q, bf16 kv
     assert lib.sparse_mla_prefill(*base(1, 2, 128, 512, 64, 1), None, 0, None) == 1  # fp8 w/o scale
