@@ -297,8 +297,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print(f"bench.py: this build runs one context-parallel rank on one GPU; "
-              f"--gpus {args.gpus} is not supported (multi-GPU sharding is design-only).",
+        print(f"bench.py measures one context-parallel rank on one GPU; "
+              f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported: the library has no "
+              f"multi-GPU path, and how the step would shard is described, not implemented.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
