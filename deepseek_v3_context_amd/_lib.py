@@ -49,6 +49,7 @@ _SIGS = {
     "cp_split_metadata": ([_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                            _i64, _p], _i32),
     "kv_rerange": ([_p, _i32, _i32, _i32, _i64, _p, _p], _i32),
+    "kv_cache_write": ([_p, _i32, _i64, _p, _p, _i32, _p, _i32, _i32, _p, _i64, _p], _i32),
     "indexer_topk_workspace_size": ([_i32, _i32], _sz),
     "indexer_topk": ([_p, _i32, _p, _p, _i32, _p, _i64, _p, _p, _p, _p, _i32, _i32,
                       _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _sz, _p], _i32),
@@ -164,6 +165,29 @@ def kv_rerange(src: torch.Tensor, slot_rows: int, num_tokens: int, cp_size: int,
                         _stream(stream))
     _check("kv_rerange", st)
     return out
+
+
+def kv_cache_write(rows: torch.Tensor, batch_idx: torch.Tensor, local_cu: torch.Tensor,
+                   page_table: torch.Tensor, page_size: int, pool: torch.Tensor,
+                   stream=None) -> torch.Tensor:
+    """Step D: store the rank's own rows (row = first axis) in the paged
+    pool, in place; returns pool."""
+    if rows.dtype != pool.dtype or tuple(rows.shape[1:]) != tuple(pool.shape[1:]):
+        raise ValueError("rows and pool must have the same dtype and row shape")
+    for name, t in (("batch_idx", batch_idx), ("local_cu", local_cu), ("page_table", page_table)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    n_req = local_cu.numel() - 1
+    if batch_idx.numel() < rows.shape[0] or n_req < 0 or page_table.dim() != 2 \
+            or page_table.shape[0] < n_req:
+        raise ValueError("batch_idx needs a request per row, local_cu n_req + 1 entries, "
+                         "page_table [n_req, max_pages]")
+    row_bytes = rows.element_size() * math.prod(rows.shape[1:])
+    st = lib.kv_cache_write(_ptr(rows), rows.shape[0], row_bytes, _ptr(batch_idx),
+                            _ptr(local_cu), n_req, _ptr(page_table), page_table.shape[1], page_size,
+                            _ptr(pool), pool.shape[0], _stream(stream))
+    _check("kv_cache_write", st)
+    return pool
 
 
 def indexer_topk_workspace_size(n_q: int, max_kv_len: int) -> int:

@@ -72,10 +72,11 @@ ds_status cp_split_metadata(const int32_t* cu_seqlens, int32_t num_reqs,
   DS_REQUIRE(num_tokens >= 0, DS_ERR_INVALID_ARG, "cp_split_metadata: num_tokens < 0");
   DS_REQUIRE(num_reqs >= 1, DS_ERR_INVALID_ARG, "cp_split_metadata: num_reqs must be >= 1");
   DS_REQUIRE(cu_seqlens != nullptr, DS_ERR_INVALID_ARG, "cp_split_metadata: cu_seqlens is NULL");
-  DS_REQUIRE(rows_src == nullptr || (rows_dst != nullptr && row_bytes > 0),
+  const int32_t n = ds_cp_local_count(num_tokens, cp_size, cp_rank);
+  // a rank that owns no token gathers no row: its (empty) rows_dst may be NULL
+  DS_REQUIRE(rows_src == nullptr || (row_bytes > 0 && (rows_dst != nullptr || n == 0)),
              DS_ERR_INVALID_ARG,
              "cp_split_metadata: row gather needs rows_dst and row_bytes > 0");
-  const int32_t n = ds_cp_local_count(num_tokens, cp_size, cp_rank);
   ds_status st = launch_split_metadata(cu_seqlens, num_reqs, num_tokens, cp_size, cp_rank,
                                        n, local_cu, batch_idx, global_idx, kv_start,
                                        kv_len, stream);
@@ -102,6 +103,32 @@ ds_status kv_rerange(const void* src, int32_t slot_rows, int32_t num_tokens,
                "kv_rerange: src and dst overlap");
   }
   return launch_rerange(src, dst, num_tokens, cp_size, slot_rows, row_bytes, stream);
+}
+
+ds_status kv_cache_write(const void* rows, int32_t n_local, int64_t row_bytes,
+                         const int32_t* batch_idx, const int32_t* local_cu, int32_t n_req,
+                         const int32_t* page_table, int32_t max_pages, int32_t page_size,
+                         void* pool, int64_t pool_rows, hipStream_t stream) {
+  DS_REQUIRE(n_local >= 0 && n_req >= 0 && max_pages >= 0 && pool_rows >= 0,
+             DS_ERR_INVALID_ARG, "kv_cache_write: negative size");
+  DS_REQUIRE(page_size >= 1, DS_ERR_INVALID_ARG, "kv_cache_write: page_size must be >= 1");
+  DS_REQUIRE(row_bytes > 0, DS_ERR_INVALID_ARG, "kv_cache_write: row_bytes must be > 0");
+  if (n_local == 0) return DS_OK;
+  DS_REQUIRE(rows != nullptr && batch_idx != nullptr && local_cu != nullptr &&
+                 (pool != nullptr || pool_rows == 0) &&
+                 (page_table != nullptr || static_cast<int64_t>(n_req) * max_pages == 0),
+             DS_ERR_INVALID_ARG, "kv_cache_write: NULL buffer");
+  if (pool_rows > 0) {
+    const char* s0 = static_cast<const char*>(rows);
+    const char* d0 = static_cast<const char*>(pool);
+    const int64_t sb = static_cast<int64_t>(n_local) * row_bytes;
+    const int64_t db = pool_rows * row_bytes;
+    DS_REQUIRE(s0 + sb <= d0 || d0 + db <= s0, DS_ERR_INVALID_ARG,
+               "kv_cache_write: rows and pool overlap");
+  }
+  if (pool_rows == 0 || static_cast<int64_t>(n_req) * max_pages == 0) return DS_OK;   // nothing maps
+  return launch_kv_cache_write(rows, n_local, row_bytes, batch_idx, local_cu, n_req,
+                               page_table, max_pages, page_size, pool, pool_rows, stream);
 }
 
 static ds_status check_indexer(const char* fn, const IndexerArgs& a) {

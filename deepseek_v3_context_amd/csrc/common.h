@@ -100,6 +100,11 @@ ds_status launch_row_gather_rr(const void* src, void* dst, int32_t n, int32_t cp
                                int32_t r, int64_t row_bytes, hipStream_t s);
 ds_status launch_rerange(const void* src, void* dst, int32_t T, int32_t cp,
                          int32_t slot_rows, int64_t row_bytes, hipStream_t s);
+ds_status launch_kv_cache_write(const void* rows, int32_t n_local, int64_t row_bytes,
+                                const int32_t* batch_idx, const int32_t* local_cu,
+                                int32_t n_req, const int32_t* page_table,
+                                int32_t max_pages, int32_t page_size, void* pool,
+                                int64_t pool_rows, hipStream_t s);
 
 struct IndexerArgs {
   const void* q_idx;

@@ -109,6 +109,69 @@ static ds_status launch_permute(const void* src, void* dst, int64_t n_rows,
   return check_launch(what);
 }
 
+// Own-KV retention: local row j, of request b = batch_idx[j] and cache
+// position p = j - local_cu[b], goes to pool row page_table[b][p / ps] * ps
+// + p % ps; a row that maps to no pool row is skipped.  One vector of V per
+// thread and step; every thread recomputes its row's destination (a few
+// cached loads) so that rows of any length need no cooperation.
+template <typename V>
+__global__ void __launch_bounds__(256)
+kv_cache_write_kernel(const V* __restrict__ src, V* __restrict__ pool, int64_t n_rows,
+                      int64_t vecs_per_row, const int32_t* __restrict__ batch_idx,
+                      const int32_t* __restrict__ local_cu, int32_t n_req,
+                      const int32_t* __restrict__ page_table, int32_t max_pages,
+                      int32_t page_size, int64_t pool_rows) {
+  const int64_t total = n_rows * vecs_per_row;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+       e < total; e += stride) {
+    const int64_t j = e / vecs_per_row;
+    const int64_t col = e - j * vecs_per_row;
+    const int32_t b = batch_idx[j];
+    if (b < 0 || b >= n_req) continue;
+    const int64_t p = j - local_cu[b];
+    if (p < 0) continue;
+    const int64_t pg = p / page_size;
+    if (pg >= max_pages) continue;
+    const int32_t page = page_table[static_cast<int64_t>(b) * max_pages + pg];
+    if (page < 0) continue;
+    const int64_t phys = static_cast<int64_t>(page) * page_size + (p - pg * page_size);
+    if (phys >= pool_rows) continue;
+    pool[phys * vecs_per_row + col] = src[e];
+  }
+}
+
+ds_status launch_kv_cache_write(const void* rows, int32_t n_local, int64_t row_bytes,
+                                const int32_t* batch_idx, const int32_t* local_cu,
+                                int32_t n_req, const int32_t* page_table,
+                                int32_t max_pages, int32_t page_size, void* pool,
+                                int64_t pool_rows, hipStream_t s) {
+  if (n_local == 0) return DS_OK;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(pool) |
+                       static_cast<uintptr_t>(row_bytes);
+  int vec = 1;
+  if ((al & 15) == 0) vec = 16;
+  else if ((al & 7) == 0) vec = 8;
+  else if ((al & 3) == 0) vec = 4;
+  const int64_t vpr = row_bytes / vec;
+  const int64_t total = static_cast<int64_t>(n_local) * vpr;
+  const int threads = 256;
+  const int64_t want = ceil_div(total, threads);
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+#define DS_KVW(V)                                                                        \
+  kv_cache_write_kernel<V><<<blocks, threads, 0, s>>>(                                   \
+      static_cast<const V*>(rows), static_cast<V*>(pool), n_local, vpr, batch_idx,       \
+      local_cu, n_req, page_table, max_pages, page_size, pool_rows)
+  switch (vec) {
+    case 16: DS_KVW(uint4); break;
+    case 8: DS_KVW(uint2); break;
+    case 4: DS_KVW(uint32_t); break;
+    default: DS_KVW(uint8_t);
+  }
+#undef DS_KVW
+  return check_launch("kv_cache_write");
+}
+
 ds_status launch_split_metadata(const int32_t* cu, int32_t B, int32_t T, int32_t cp,
                                 int32_t r, int32_t n, int32_t* local_cu,
                                 int32_t* batch_idx, int32_t* global_idx,

@@ -8,6 +8,8 @@
  *   3.+4. indexer_topk     ReLU-weighted indexer scores + per-query top-k
  *   5. sparse_mla_prefill / sparse_mla_decode
  *                          latent attention over the selected rows only
+ *   D. kv_cache_write      the rank keeps its own tokens' KV in the paged
+ *                          cache pool for the decode steps
  *
  * Sources (cited per entry point below):
  *   [RFC]   "[RFC]: Parallel strategy for Deepseek v3.2 like models"
@@ -100,8 +102,9 @@ int32_t ds_cp_local_count(int64_t num_tokens, int32_t cp_size, int32_t cp_rank);
  *   rows_src   [num_tokens, row_bytes] dev, or NULL: optional row gather,
  *   rows_dst   [n, row_bytes] dev        rows_dst[j] = rows_src[g_j]
  * Errors: INVALID_ARG for cp_size < 1, cp_rank outside [0, cp_size),
- * num_tokens < 0, num_reqs < 1, NULL cu_seqlens, rows_src without
- * rows_dst or row_bytes <= 0.
+ * num_tokens < 0, num_reqs < 1, NULL cu_seqlens, rows_src with
+ * row_bytes <= 0, or without rows_dst on a rank that owns tokens (a rank
+ * with none may pass NULL).
  * ------------------------------------------------------------------- */
 ds_status cp_split_metadata(const int32_t* cu_seqlens, int32_t num_reqs,
                             int32_t num_tokens, int32_t cp_size,
@@ -257,6 +260,39 @@ ds_status sparse_mla_decode(const void* q, ds_dtype q_dtype, const void* kv,
                             int32_t d_rope, int32_t topk, float sm_scale,
                             void* out, ds_dtype out_dtype, float* lse,
                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Step D: the rank keeps its own tokens' KV in the paged cache pool.
+ * [BLOG] section 4 part 3, step D: after attention the gathered global KV
+ * is dropped, and each rank keeps only the KV of the tokens it owns (rank 1
+ * keeps K1, K5 of the 8-token example) in the device cache pool, for the
+ * decode steps.
+ *
+ *   rows       [n_local, row_bytes] dev   the rank's own rows in local order
+ *                                         (cp_split_metadata's rows_dst)
+ *   batch_idx  [n_local] dev int32        request of each local row
+ *   local_cu   [n_req + 1] dev int32      first local row of each request
+ *                                         (both from cp_split_metadata)
+ *   page_table [n_req, max_pages] dev int32  page ids of each request's
+ *                                         cache; -1 = not mapped
+ *   pool       [pool_rows, row_bytes] dev written in place
+ * Local row j, of request b = batch_idx[j] and cache position
+ * p = j - local_cu[b], is copied to pool row
+ * page_table[b][p / page_size] * page_size + p % page_size: the mapping the
+ * decode calls read through.  A row is not written when b is outside
+ * [0, n_req), p < 0, p / page_size >= max_pages, the page id is negative or
+ * the pool row is >= pool_rows; nothing else in the pool changes.
+ * Dtype-agnostic (moves bytes: the pool keeps the rows' storage format).
+ * rows and pool must not overlap.  If the table maps two positions to one
+ * pool row, either row may be kept.
+ * Errors: INVALID_ARG for n_local, n_req, max_pages or pool_rows < 0,
+ * page_size < 1, row_bytes <= 0, NULL buffers that are needed (n_local > 0),
+ * overlapping rows and pool.
+ * ------------------------------------------------------------------- */
+ds_status kv_cache_write(const void* rows, int32_t n_local, int64_t row_bytes,
+                         const int32_t* batch_idx, const int32_t* local_cu, int32_t n_req,
+                         const int32_t* page_table, int32_t max_pages, int32_t page_size,
+                         void* pool, int64_t pool_rows, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -81,6 +81,31 @@ def _p(x=256):
     return ctypes.c_void_p(x)
 
 
+def test_kv_cache_write_rejects_bad_arguments_before_launch():
+    lib = ctypes.CDLL(ds.LIB_PATH)
+    f = lib.kv_cache_write
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    p = ctypes.c_void_p
+
+    def call(n_local=4, row_bytes=16, n_req=1, max_pages=2, page_size=4, pool_rows=8,
+             rows=p(256), bi=p(4096), lcu=p(8192), pt=p(12288), pool=p(1 << 20)):
+        return f(rows, n_local, row_bytes, bi, lcu, n_req, pt, max_pages, page_size, pool,
+                 pool_rows, None)
+
+    assert call(n_local=-1) == 1
+    assert call(page_size=0) == 1
+    assert call(row_bytes=0) == 1
+    assert call(pool_rows=-1) == 1
+    assert call(rows=None) == 1
+    assert call(pt=None) == 1
+    assert call(rows=p(1 << 20), pool=p((1 << 20) + 32)) == 1          # overlap
+    assert call(n_local=0, rows=None, bi=None, lcu=None, pt=None, pool=None) == 0
+    assert call(pool_rows=0, pool=None) == 0                             # nothing maps
+
+
 def test_indexer_rejects_unsupported_and_small_workspace():
     args = lambda q_dt, k_dt, h, d, topk, ws: (  # noqa: E731
         _p(), q_dt, _p(), _p(), k_dt, None, 100, _p(), _p(), None, None, 0, 0, 0,

@@ -1,0 +1,92 @@
+"""GPU parity of kv_cache_write (the rank keeps its own KV in the paged
+pool) against oracle/kv_cache.py: bit-exact, on the metadata the split
+kernel itself produces."""
+
+import numpy as np
+import pytest
+import torch
+
+import deepseek_v3_context_amd as ds
+from oracle import kv_cache as kc
+from oracle import round_robin_cp as rr
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _pages(own, page_size, rng, spare=3, holes=False):
+    """Random page table for each request's own tokens (a shuffled pool
+    with a few spare pages); with holes, every third page is unmapped."""
+    counts = [-(-int(c) // page_size) for c in own]
+    width = max(counts + [1])
+    perm = rng.permutation(sum(counts) + spare).astype(np.int32)
+    table = np.full((len(own), width), -1, dtype=np.int32)
+    off = 0
+    for b, k in enumerate(counts):
+        table[b, :k] = perm[off: off + k]
+        off += k
+    if holes:
+        table[:, ::3] = -1
+    return table, (sum(counts) + spare) * page_size
+
+
+def _case(cu, cp, r, row_shape, np_dtype, page_size, seed, holes=False, short_pool=False):
+    print(f"[kv_cache_write] cu={list(cu)[:4]}.. cp={cp} r={r} row={row_shape} "
+          f"ps={page_size} holes={holes} short={short_pool}", flush=True)
+    rng = np.random.default_rng(seed)
+    cu = np.asarray(cu, dtype=np.int32)
+    T = int(cu[-1])
+    meta_h = rr.split_metadata(cu, cp, r)
+    own = np.diff(meta_h["local_cu"])
+    table, pool_rows = _pages(own, page_size, rng, holes=holes)
+    if short_pool:
+        pool_rows = max(pool_rows - 2 * page_size - 1, 0)
+    full = rng.integers(0, 255, size=(T,) + row_shape, dtype=np.uint8).view(np_dtype) \
+        if np_dtype == np.uint8 else rng.integers(0, 1 << 15, size=(T,) + row_shape).astype(np_dtype)
+    pool0 = rng.integers(0, 1 << 7, size=(pool_rows,) + row_shape).astype(np_dtype)
+    # device side: the split kernel gathers the rank's rows and its metadata
+    src = torch.from_numpy(full).to(DEV)
+    meta = ds.cp_split_metadata(torch.from_numpy(cu).to(DEV), T, cp, r, rows_src=src)
+    pool = torch.from_numpy(pool0).to(DEV)
+    ds.kv_cache_write(meta["rows"], meta["batch_idx"], meta["local_cu"],
+                      torch.from_numpy(table).to(DEV), page_size, pool)
+    got = pool.cpu().numpy()
+    # oracle side: its own split of the same rows
+    rows_h = rr.split_rows(full, cp, r) if len(meta_h["batch_idx"]) else full[:0]
+    want = kc.own_kv_cache_write(rows_h, meta_h["batch_idx"], meta_h["local_cu"], table,
+                                 page_size, pool0)
+    assert got.shape == want.shape
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+    return got, want
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 64])
+@pytest.mark.parametrize("row_shape,np_dtype", [((576,), np.int16), ((128,), np.int16),
+                                                ((3,), np.uint8)])
+def test_small_batches_every_row(page_size, row_shape, np_dtype):
+    _case([0, 37, 41, 130, 200], 4, 2, row_shape, np_dtype, page_size, seed=page_size)
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_unmapped_pages_and_a_short_pool_leave_the_rest_alone(page_size):
+    _case([0, 300, 301, 700], 4, 1, (576,), np.int16, page_size, seed=7, holes=True,
+          short_pool=True)
+
+
+def test_rank_without_tokens_writes_nothing():
+    got, want = _case([0, 3], 8, 5, (576,), np.int16, 64, seed=3)
+    assert np.array_equal(got, want)
+
+
+def test_full_size_8000_token_prefill_rank0():
+    _case([0, 8000], 8, 0, (576,), np.int16, 64, seed=11)
+
+
+def test_full_size_65536_token_prefill_rank3_and_indexer_keys():
+    _case([0, 65536], 8, 3, (576,), np.int16, 64, seed=12)
+    _case([0, 65536], 8, 3, (128,), np.uint8, 64, seed=13)   # fp8 indexer keys: 128 B rows
+
+
+def test_six_requests_25305_tokens_rank5():
+    cu = [0, 1000, 5000, 5001, 12000, 20000, 25305]
+    _case(cu, 8, 5, (576,), np.int16, 64, seed=14)
