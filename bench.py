@@ -293,6 +293,47 @@ def cpu_baseline(wl, st, kv_len_host, seconds):
                       f"queries), indexer + top-k + sparse MLA in float64 NumPy, {dt:.1f} s"}
 
 
+def own_kv_cache_write(wl, torch, ds, st, dev, steps):
+    """The rank keeping its own tokens' latent KV and indexer keys in a paged
+    pool (64-row pages, the decode pool's), after the timed region and
+    outside the step.  `steps` back-to-back calls of each sit between one
+    HIP event pair (a pair per call would mostly time the events, the call
+    being a few microseconds).  The host takes longer to issue a call than
+    the device to run it, so a bounded spin kernel holds the stream until
+    every call is queued: the pair then times the device running them back
+    to back.  Bytes per call: each own row read once and written once."""
+    from synth import draw_page_table
+
+    print("[bench] own-KV cache write", file=sys.stderr, flush=True)
+    m = st["meta"]
+    lcu = m["local_cu"].cpu().numpy()
+    n = int(lcu[-1])
+    table, pool_rows = draw_page_table(lcu[1:] - lcu[:-1], 64, seed=wl.seed)
+    table_d = torch.from_numpy(table).to(dev)
+    r, slot = wl.cp_rank, st["slot"]
+    srcs = {"kv_cache_write(latent)": st["kv_cat"][r * slot: r * slot + n],
+            "kv_cache_write(indexer_k)": st["ki_cat"][r * slot: r * slot + n]}
+    pools = {k: torch.empty((pool_rows,) + tuple(v.shape[1:]), dtype=v.dtype, device=dev)
+             for k, v in srcs.items()}
+    per_call = {}
+    for k, v in srcs.items():
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(60000 * steps)   # ~25 us of device time per queued call
+        ev0.record()
+        for _ in range(steps):
+            ds.kv_cache_write(v, m["batch_idx"], m["local_cu"], table_d, 64, pools[k])
+        ev1.record()
+        torch.cuda.synchronize()
+        per_call[k] = ev0.elapsed_time(ev1) / steps
+    out = {}
+    for k, ms in per_call.items():
+        nbytes = 2 * n * srcs[k].element_size() * srcs[k][0].numel() if n else 0
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[k] = {"avg_us": round(ms * 1e3, 2), "bytes": nbytes, "gbs": round(gbs, 1),
+                  "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -396,6 +437,8 @@ def main():
         "kernel_timing": "kernels: separate pass, HIP events around every call; "
                          "roofline: timed region, events around the dominant call only",
     }
+    if wl.kind == "prefill":
+        line["outside_step"] = own_kv_cache_write(wl, torch, ds, st, dev, args.steps)
     if args.cpu_seconds > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, st, kv_len_host, args.cpu_seconds)

@@ -9,4 +9,4 @@ here.
 """
 
 from .workloads import WORKLOADS, Workload, get  # noqa: F401
-from .draw import draw_prefill, draw_decode  # noqa: F401
+from .draw import draw_prefill, draw_decode, draw_page_table  # noqa: F401

@@ -24,7 +24,7 @@ from .workloads import Workload
 
 _CHUNK = 1 << 22
 _IDS = {"q_idx": 1, "w": 2, "k_idx": 3, "q": 4, "kv": 5, "input_ids": 6,
-        "lengths": 7, "pages": 8}
+        "lengths": 7, "pages": 8, "own_pages": 9}
 FP8_BLOCK_ROWS = 128
 E4M3_MAX = 448.0
 
@@ -111,6 +111,23 @@ def draw_prefill(wl: Workload, n_local: int) -> dict:
     kv = _normal(s, "kv", (T, wl.d_qk), wl.d_qk ** -0.5)
     out["kv"], out["kv_scale"] = _store(kv, wl.kv_fmt)
     return out
+
+
+def draw_page_table(counts, page_size: int, seed: int, spare: int = 0):
+    """A paged pool holding ``counts[b]`` rows for request ``b``: every
+    request gets ceil(counts[b] / page_size) pages of a seeded random
+    permutation of the pool's pages (plus ``spare`` unused ones).  Returns
+    (page_table [n_req, max_pages] int32 with -1 past a request's pages,
+    pool_rows)."""
+    pages = [-(-int(c) // page_size) for c in counts]
+    n_pages = int(sum(pages)) + spare
+    perm = _stream(seed, "own_pages").permutation(n_pages).astype(np.int32)
+    table = np.full((len(pages), max(pages + [1])), -1, dtype=np.int32)
+    off = 0
+    for b, k in enumerate(pages):
+        table[b, :k] = perm[off: off + k]
+        off += k
+    return table, n_pages * page_size
 
 
 def draw_decode(wl: Workload) -> dict:

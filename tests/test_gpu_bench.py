@@ -37,5 +37,9 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline():
     assert roof["unit"] in ("GB/s", "TFLOP/s")
     assert 0 < roof["frac"] <= 1 and roof["peak"] > 0
     assert roof["achieved"] == pytest.approx(roof["frac"] * roof["peak"], rel=1e-2)
+    # the own-KV cache write is measured after the timed region, outside the step
+    for k in ("kv_cache_write(latent)", "kv_cache_write(indexer_k)"):
+        w = d["outside_step"][k]
+        assert w["avg_us"] > 0 and w["bytes"] > 0 and 0 < w["frac"] <= 1
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
