@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="after the warm-up steps, keep running untimed steps for at least this "
                          "long so that the GPU clocks have ramped (0 = off)")
+    ap.add_argument("--all-ranks", action="store_true",
+                    help="prefill: after the measurement, also time the step on every rank's "
+                         "share and report the per-rank spread (rank_balance)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -334,6 +337,39 @@ def own_kv_cache_write(wl, torch, ds, st, dev, steps):
     return out
 
 
+def rank_balance(wl, torch, ds, dev, args):
+    """The step on every rank's share of the same prefill (round-robin
+    split), each rank set up on its own, warmed up and timed like the main
+    measurement (K steps between two device synchronisations, no events).
+    spread = (max - min) / mean of the per-rank step times."""
+    import dataclasses
+
+    ms, nq = [], []
+    for r in range(wl.cp_size):
+        print(f"[bench] rank balance: rank {r}", file=sys.stderr, flush=True)
+        wr = dataclasses.replace(wl, cp_rank=r)
+        st = setup_prefill(wr, torch, ds, dev)
+        none = Timed(torch, only=())
+        t_end = time.perf_counter() + max(args.settle_ms, 0.0) * 1e-3
+        for i in range(max(args.warmup, 1)):
+            prefill_step(wr, ds, st, none)
+        while time.perf_counter() < t_end:
+            prefill_step(wr, ds, st, none)
+            torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            prefill_step(wr, ds, st, none)
+        torch.cuda.synchronize()
+        ms.append(round((time.perf_counter() - t0) / args.steps * 1e3, 4))
+        nq.append(st["n"])
+        del st
+        torch.cuda.empty_cache()
+    mean = sum(ms) / len(ms)
+    return {"split": "round-robin", "ms_per_step": ms, "queries": nq,
+            "spread": round((max(ms) - min(ms)) / mean, 4)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -439,6 +475,8 @@ def main():
     }
     if wl.kind == "prefill":
         line["outside_step"] = own_kv_cache_write(wl, torch, ds, st, dev, args.steps)
+        if args.all_ranks:
+            line["rank_balance"] = rank_balance(wl, torch, ds, dev, args)
     if args.cpu_seconds > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, st, kv_len_host, args.cpu_seconds)
