@@ -90,3 +90,59 @@ def test_full_size_65536_token_prefill_rank3_and_indexer_keys():
 def test_six_requests_25305_tokens_rank5():
     cu = [0, 1000, 5000, 5001, 12000, 20000, 25305]
     _case(cu, 8, 5, (576,), np.int16, 64, seed=14)
+
+
+# ------------------------------------------------------------ prefill -> decode
+
+@pytest.mark.parametrize("name", ["small_decode_paged", "small_decode_paged_fp8"])
+def test_decode_reads_what_the_prefill_rank_kept(name):
+    """The decode path on a pool that kv_cache_write filled from each
+    request's rows in logical order (a cp 1 prefill keeps every token): the
+    pool matches the drawn one at every mapped row and is untouched
+    elsewhere, and decode output passes the decode parity gates."""
+    from synth import draw_decode, get
+    from oracle import pipeline as opl
+    from tests import gpu_path as gp
+    from tests import test_gpu_parity as tgp
+
+    wl = get(name)
+    inp = draw_decode(wl)
+    print(f"[kv_cache_write -> decode] {name}", flush=True)
+    lengths = inp["lengths"].astype(np.int64)
+    table, ps = inp["page_table"], wl.page_size
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    phys = np.concatenate([sa_rows(table, ps, b, int(L)) for b, L in enumerate(lengths)])
+    meta = None
+    pools = {}
+    for key in ("kv", "k_idx"):
+        drawn = np.ascontiguousarray(inp[key])
+        nrow = drawn.shape[0]
+        as_bytes = drawn.reshape(nrow, -1).view(np.uint8)          # rows as raw bytes
+        logical = torch.from_numpy(np.ascontiguousarray(as_bytes[phys])).to(DEV)
+        meta = ds.cp_split_metadata(torch.from_numpy(cu).to(DEV), T, 1, 0, rows_src=logical)
+        # all-ones bytes: NaN in bf16 and in e4m3fn, so a read of an unwritten row shows
+        pool = torch.full(as_bytes.shape, 0xFF, dtype=torch.uint8, device=DEV)
+        ds.kv_cache_write(meta["rows"], meta["batch_idx"], meta["local_cu"],
+                          torch.from_numpy(table).to(DEV), ps, pool)
+        got = pool.cpu().numpy()
+        mapped = np.zeros(nrow, bool)
+        mapped[phys] = True
+        assert np.array_equal(got[mapped], as_bytes[mapped])
+        assert (got[~mapped] == 0xFF).all()
+        pools[key] = got.view(drawn.dtype).reshape(drawn.shape)
+    inp2 = dict(inp, kv=pools["kv"], k_idx=pools["k_idx"])
+    g = gp.run_decode(wl, inp2)
+    dmeta = opl.decode_metadata(inp["lengths"])
+    rows = list(range(wl.n_req))
+    sel = opl.indexer_topk_rows(rows, dmeta, inp["q_idx"], wl.act_fmt, inp["w"], inp["k_idx"],
+                                wl.kv_fmt, inp["k_idx_scale"], wl.topk,
+                                page_table=table, page_size=ps)
+    tgp._check_rows(wl, g, sel, rows, inp, inp["kv"], inp["kv_scale"])
+
+
+def sa_rows(table, page_size, b, L):
+    """Physical pool rows of request b's positions 0..L-1 (test-side data
+    preparation: the decode pool layout the workload generator drew)."""
+    p = np.arange(L)
+    return table[b, p // page_size].astype(np.int64) * page_size + p % page_size
