@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_t8000_cp8")
+    ap.add_argument("--workload", default="prefill_t65536_cp8_fp8")
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="after the warm-up steps, keep running untimed steps for at least this "
                          "long so that the GPU clocks have ramped (0 = off)")
@@ -80,6 +80,20 @@ class Timed:
 
     def avg_ms(self):
         return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.events.items()}
+
+
+def rank_max_kv_len(cu_seqlens, cp, r):
+    """Longest causal key range of rank r's queries: per request, the
+    rank's last token g (g = r mod cp) sees positions cu[b] .. g."""
+    best = 0
+    cu = [int(x) for x in cu_seqlens]
+    for lo, hi in zip(cu[:-1], cu[1:]):
+        if hi <= lo:
+            continue
+        g = hi - 1 - ((hi - 1 - r) % cp)
+        if g >= lo:
+            best = max(best, g - lo + 1)
+    return best
 
 
 def setup_prefill(wl, torch, ds, dev):
@@ -128,8 +142,11 @@ def setup_prefill(wl, torch, ds, dev):
                   "kv_len": torch.empty(n, **i32), "rows": torch.empty(n, **i32)}
     st["kv"] = torch.empty((T, wl.d_qk), dtype=kv_cat.dtype, device=dev)
     st["ki"] = torch.empty((T, wl.d_idx), dtype=ki_cat.dtype, device=dev)
-    st["max_len"] = T
-    st["scores"] = torch.empty((n, ((T + 63) // 64) * 64), dtype=torch.float32, device=dev)
+    # the longest causal range among the rank's queries (host-known from the
+    # request lengths): it sizes the score rows and picks the top-k variant
+    st["max_len"] = rank_max_kv_len(inp["cu_seqlens"], cp, r)
+    st["scores"] = torch.empty((n, ((st["max_len"] + 63) // 64) * 64), dtype=torch.float32,
+                               device=dev)
     st["topk_idx"] = torch.empty((n, wl.topk), **i32)
     st["out"] = torch.empty((n, wl.n_heads, wl.d_latent), dtype=torch.bfloat16 if wl.act_fmt != "f32" else torch.float32, device=dev)
     st["lse"] = torch.empty((n, wl.n_heads), dtype=torch.float32, device=dev)
@@ -266,11 +283,20 @@ def cpu_baseline(wl, st, kv_len_host, seconds):
     from oracle import pipeline as opl
     from oracle import round_robin_cp as orr
 
+    # multithreaded BLAS with the thread count it is configured for: the
+    # affinity mask can list every CPU of the host while the process's CPU
+    # share is smaller (OMP_NUM_THREADS and the like name that share), and
+    # raising the BLAS to the mask's size oversubscribes the share
+    visible = len(os.sched_getaffinity(0))
+    cores, blas = visible, "unknown BLAS"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
+            cores = min(visible, int(info[0].get("num_threads", visible)))
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        pass
     inp = st["inp"]
     n = st["n"]
     if wl.kind == "prefill":
@@ -291,7 +317,8 @@ def cpu_baseline(wl, st, kv_len_host, seconds):
             break
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "query tokens/s", "cores": int(cores),
-            "kind": "oracle",
+            "cpus_visible": visible, "kind": "oracle", "blas": blas,
+            "label": "plain NumPy oracle, not an optimized CPU baseline",
             "sample": f"{done} of {n} query rows (seeded random order over the rank's "
                       f"queries), indexer + top-k + sparse MLA in float64 NumPy, {dt:.1f} s"}
 
@@ -335,6 +362,28 @@ def own_kv_cache_write(wl, torch, ds, st, dev, steps):
         out[k] = {"avg_us": round(ms * 1e3, 2), "bytes": nbytes, "gbs": round(gbs, 1),
                   "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     return out
+
+
+def cold_steps(wl, torch, ds, st, step, steps):
+    """The step with the Infinity Cache (MALL) flushed before each one: a
+    512 MB scratch write between steps, outside the events; one event pair
+    around every step."""
+    print("[bench] cold-cache steps", file=sys.stderr, flush=True)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    none = Timed(torch, only=())
+    ms = []
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        step(wl, ds, st, none)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms.append(ev0.elapsed_time(ev1))
+    del flush
+    ms.sort()
+    return {"ms_per_step_median": round(ms[len(ms) // 2], 4), "ms_per_step_mean": round(sum(ms) / len(ms), 4),
+            "steps": steps, "flush": "512 MB device write before every step, outside the events"}
 
 
 def rank_balance(wl, torch, ds, dev, args):
@@ -472,7 +521,11 @@ def main():
                     "settle_ms": round(settle_ms, 1), "per_call_pass_steps": args.steps},
         "kernel_timing": "kernels: separate pass, HIP events around every call; "
                          "roofline: timed region, events around the dominant call only",
+        "kernel_gbs": "algorithmic bytes per call / time; sparse_mla counts every selected "
+                      "row once per query that selects it (gathered bytes, not HBM traffic)",
     }
+    if wl.kind == "decode":
+        line["cold_cache"] = cold_steps(wl, torch, ds, st, step, args.steps)
     if wl.kind == "prefill":
         line["outside_step"] = own_kv_cache_write(wl, torch, ds, st, dev, args.steps)
         if args.all_ranks:

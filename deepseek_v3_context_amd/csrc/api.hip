@@ -2,6 +2,7 @@
 // (before any launch), workspace sizing and dispatch to the kernels.
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "common.h"
@@ -25,14 +26,17 @@ ds_status check_launch(const char* what) {
 }
 
 int32_t device_cu_count() {
-  static int32_t cached[64] = {};
+  static std::atomic<int32_t> cached[kMaxDevices] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < kMaxDevices) {
+    const int32_t c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
-  if (dev < 64) cached[dev] = n;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -311,7 +315,7 @@ ds_status sparse_mla_prefill(const void* q, ds_dtype q_dtype, const void* kv,
                "sparse_mla_prefill: fp8 kv needs sparse_mla_prefill_workspace_size() bytes of workspace");
     DS_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, DS_ERR_INVALID_ARG,
                "sparse_mla_prefill: workspace must be 256-byte aligned");
-    st = launch_widen_fp8_rows(kv, kv_scale, kv_rows, ws, stream);
+    st = launch_widen_fp8_rows(kv, kv_scale, a.scale_shift, kv_rows, ws, stream);
     if (st != DS_OK) return st;
     a.kv = ws;
     a.kv_dtype = DS_BF16;

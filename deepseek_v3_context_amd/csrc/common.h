@@ -29,6 +29,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kMaxDevices = 64;   // per-device host caches
 constexpr int kFp8BlockRows = 128;
 
 // ------------------------------------------------------------ conversions
@@ -146,8 +147,8 @@ struct TopkArgs {
 ds_status launch_topk(const TopkArgs& a, hipStream_t s);
 // fp8 latent rows (576 codes, scale per 128 rows) -> bf16 rows (code * scale)
 constexpr int kMlaWidenedRowBytes = 576 * 2;
-ds_status launch_widen_fp8_rows(const void* codes, const float* scale, int64_t rows, void* out,
-                                hipStream_t s);
+ds_status launch_widen_fp8_rows(const void* codes, const float* scale, int32_t scale_shift,
+                                int64_t rows, void* out, hipStream_t s);
 // Rows longer than this are selected in two phases when there are few of
 // them (their candidates need topk_two_phase_bytes() of workspace).
 constexpr int32_t kTopkSegLen = 8192;
@@ -175,6 +176,7 @@ struct MlaArgs {
   float* lse;
   int32_t n_splits;   // > 1: split each query's rows (decode variant)
   void* ws;           // partials for n_splits > 1
+  int32_t scale_shift = 7;   // fp8 kv: scale of row r is kv_scale[r >> scale_shift]
 };
 ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s);
 size_t mla_partials_bytes(int32_t n_q, int32_t n_heads, int32_t d_latent,

@@ -11,26 +11,18 @@
 //   out[j,h,:] = sum_s softmax_s(sm_scale * <q[j,h,:], kv[s,:]>) kv[s,:d_latent]
 //   lse[j,h]   = log sum_s exp(sm_scale * <q[j,h,:], kv[s,:]>).
 //
-// bf16/fp8 path (d_latent 512, d_rope 64, heads a multiple of 32): one
-// workgroup per (query, split of its selected rows) with one wave per 32
-// heads (two groups of 16 that share every K and V fragment read).  The selected rows are gathered 64 at a time into LDS (one copy
-// serves all heads, as key for QK and as value for PV), and every wave runs
-// a flash-style loop with MFMA v_mfma_f32_16x16x32_bf16:
-//   S^T[key, head] = K[key, :] . Q[head, :]     A = K (LDS), B = Q (regs)
-//   O^T[c, head]  += V^T[c, key] . P^T[key, head]
-// The transposed form makes the QK output layout (one head per lane, four
-// keys per lane) exactly the B operand layout PV needs, so P never leaves
-// registers; O^T (2 x 16 heads x 512) stays in 256 accumulator registers
-// per lane and each lane owns one head per group, so the online-softmax
-// rescale is one scalar per lane and group.  fp8 rows are widened to bf16 exactly in LDS and their
-// per-block scale multiplies the logits of that key and its softmax weight
-// before PV (both in fp32).
-//
+// Kernels (d_latent 512, d_rope 64; 32, 64 or 128 heads):
+//   * mla_bf16_wide_kernel: bf16 rows (and fp8 prefill rows, widened once
+//     per call into the workspace).  One workgroup per (query, split of its
+//     selected rows), one wave per 32 heads and per SIMD; 32-row tiles of
+//     the selected rows are gathered into LDS by DMA and serve all heads as
+//     key (QK) and value (PV) on v_mfma_f32_16x16x32_bf16.
+//   * mla_fp8_kernel: fp8 rows read in place (decode pools), widened to
+//     bf16 exactly in LDS; the row scales are applied in fp32.
+//   * mla_f32_kernel: the all-fp32 path of the tiny workload.
 // Decode (few queries) splits each query's selected rows over several
 // workgroups that write unnormalised partial outputs with their running
-// max and sum; a combine kernel merges them by log-sum-exp.
-#include <stdlib.h>
-
+// max and sum; mla_combine_kernel merges them by log-sum-exp.
 #include <type_traits>
 #include <utility>
 
@@ -163,21 +155,28 @@ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * kMlaLdsRow + (c << 4);
 }
 
+// ------------------------------------------------------ fp8 KV (decode)
+// One workgroup of n_heads/16 waves per (query, split of its rows); wave w
+// owns heads 16w .. 16w+15.  The split's rows are gathered 64 at a time
+// into LDS and widened to bf16 exactly (unit scale: every e4m3fn code is a
+// bf16 value); the per-block scale of a row multiplies its logits (before
+// the softmax) and its softmax weight (before PV), both in fp32, so the
+// arithmetic is on the codes exactly as stored.
+//   S^T[key, head] = K[key, :] . Q[head, :]     A = K (LDS), B = Q (regs)
+//   O^T[c, head]  += V^T[c, key] . P^T[key, head]
+// The transposed form makes the QK output layout (one head per lane, four
+// keys per lane) exactly the B operand layout PV needs, so P never leaves
+// registers; O^T (16 heads x 512) is 128 accumulator registers per lane and
+// each lane owns one head, so a rescale is one scalar per lane.
+//
 // Lazy rescaling: the running reference max of a head only moves when a
 // tile's max exceeds it by more than 2^kRescaleLog2, so that exp2 of any
-// logit minus the reference stays below 2^8 and the 256-register output
-// accumulator is rescaled only on the rare tiles that raise the max.
+// logit minus the reference stays below 2^8 and the output accumulator is
+// rescaled only on the rare tiles that raise the max.
 constexpr float kRescaleLog2 = 8.f;
 
-// 16-head groups per wave.
-#ifndef DS32CP_MLA_GROUPS
-#define DS32CP_MLA_GROUPS 1
-#endif
-constexpr int kMlaGroups = DS32CP_MLA_GROUPS;
-
-template <bool kFp8, bool kTrV, int kG>
-__global__ void __launch_bounds__(kWave * 8 / kG)
-mla_mfma_kernel(MlaArgs a, int32_t keys_per_split) {
+__global__ void __launch_bounds__(kWave * 8)
+mla_fp8_kernel(MlaArgs a, int32_t keys_per_split) {
   __shared__ __align__(16) uint8_t tile[kMlaTile * kMlaLdsRow];
   __shared__ int32_t rows[kMlaTile];
   __shared__ float kscale[kMlaTile];
@@ -190,35 +189,29 @@ mla_mfma_kernel(MlaArgs a, int32_t keys_per_split) {
   const int wave = tid >> 6;
   const int nthreads = blockDim.x;
   const int grp = lane >> 4;                      // 0..3
-  // this lane's heads: one per 16-head group of the wave
-  const int hbase = wave * 16 * kG + (lane & 15);
+  const int h = wave * 16 + (lane & 15);          // this lane's head
 
   const int32_t s_begin = split * keys_per_split;
   int32_t s_end = s_begin + keys_per_split;
   s_end = s_end < a.topk ? s_end : a.topk;
 
   // Q^T fragments (B operand): head h, dims 32*ks + 8*grp + 0..7.
-  bf16x8 qf[kG][kMlaKSteps];
-#pragma unroll
-  for (int g2 = 0; g2 < kG; ++g2) {
+  bf16x8 qf[kMlaKSteps];
+  {
     const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        (static_cast<int64_t>(j) * a.n_heads + hbase + 16 * g2) * kMlaD + grp * 8;
+                        (static_cast<int64_t>(j) * a.n_heads + h) * kMlaD + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < kMlaKSteps; ++ks)
-      qf[g2][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
   }
 
-  f32x4 o[kG][kMlaCBlocks];
-  float m_ref[kG];   // reference max (log2 domain)
-  float l_run[kG];   // sum of exp2(logit - m_ref)
+  f32x4 o[kMlaCBlocks];
+  float m_ref = -INFINITY;   // reference max (log2 domain)
+  float l_run = 0.f;         // sum of exp2(logit - m_ref)
 #pragma unroll
-  for (int g2 = 0; g2 < kG; ++g2) {
-    m_ref[g2] = -INFINITY;
-    l_run[g2] = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < kMlaCBlocks; ++cb) o[g2][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int cb = 0; cb < kMlaCBlocks; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float scale2 = a.sm_scale * kLog2e;
+  const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
 
   for (int32_t t0 = s_begin; t0 < s_end; t0 += kMlaTile) {
     // ---- gather the tile's rows into LDS
@@ -227,7 +220,7 @@ mla_mfma_kernel(MlaArgs a, int32_t keys_per_split) {
       int32_t r = s < s_end ? a.topk_idx[static_cast<int64_t>(j) * a.topk + s] : -1;
       if (r >= a.kv_rows) r = -1;
       rows[tid] = r;
-      kscale[tid] = (kFp8 && r >= 0) ? a.kv_scale[r / kFp8BlockRows] : 1.f;
+      kscale[tid] = r >= 0 ? a.kv_scale[r >> a.scale_shift] : 1.f;
       const uint64_t b = __ballot(r >= 0);
       if (tid == 0) any_valid = b != 0ull;
     }
@@ -236,239 +229,147 @@ mla_mfma_kernel(MlaArgs a, int32_t keys_per_split) {
       __syncthreads();
       continue;
     }
-    if constexpr (kFp8) {
-      constexpr int kPieces = kMlaTile * (kMlaD / 16);   // 16 codes per piece
-      for (int piece = tid; piece < kPieces; piece += nthreads) {
-        const int r = piece / (kMlaD / 16);
-        const int c8 = piece - r * (kMlaD / 16);
-        const int32_t row = rows[r];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row >= 0)
-          v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv) +
-                                              static_cast<int64_t>(row) * kMlaD + c8 * 16);
-        const uint2 a0 = fp8x4_to_bf16x4(v.x), a1 = fp8x4_to_bf16x4(v.y);
-        const uint2 a2 = fp8x4_to_bf16x4(v.z), a3 = fp8x4_to_bf16x4(v.w);
-        *reinterpret_cast<uint4*>(&tile[tile_off(r, 2 * c8)]) = make_uint4(a0.x, a0.y, a1.x, a1.y);
-        *reinterpret_cast<uint4*>(&tile[tile_off(r, 2 * c8 + 1)]) = make_uint4(a2.x, a2.y, a3.x, a3.y);
-      }
-    } else {
-      constexpr int kPieces = kMlaTile * kMlaRowChunks;
-      for (int piece = tid; piece < kPieces; piece += nthreads) {
-        const int r = piece / kMlaRowChunks;
-        const int c = piece - r * kMlaRowChunks;
-        const int32_t row = rows[r];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row >= 0)
-          v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv) +
-                                              static_cast<int64_t>(row) * kMlaRowBytes + c * 16);
-        *reinterpret_cast<uint4*>(&tile[tile_off(r, c)]) = v;
-      }
+    constexpr int kPieces = kMlaTile * (kMlaD / 16);   // 16 codes per piece
+    for (int piece = tid; piece < kPieces; piece += nthreads) {
+      const int r = piece / (kMlaD / 16);
+      const int c8 = piece - r * (kMlaD / 16);
+      const int32_t row = rows[r];
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row >= 0)
+        v = *reinterpret_cast<const uint4*>(kv + static_cast<int64_t>(row) * kMlaD + c8 * 16);
+      const uint2 a0 = fp8x4_to_bf16x4(v.x), a1 = fp8x4_to_bf16x4(v.y);
+      const uint2 a2 = fp8x4_to_bf16x4(v.z), a3 = fp8x4_to_bf16x4(v.w);
+      *reinterpret_cast<uint4*>(&tile[tile_off(r, 2 * c8)]) = make_uint4(a0.x, a0.y, a1.x, a1.y);
+      *reinterpret_cast<uint4*>(&tile[tile_off(r, 2 * c8 + 1)]) = make_uint4(a2.x, a2.y, a3.x, a3.y);
     }
     __syncthreads();
 
-    // ---- S^T = K Q^T for 4 blocks of 16 keys, both head groups
-    f32x4 st[kG][4];
+    // ---- S^T = K Q^T for 4 blocks of 16 keys
+    f32x4 st[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int g2 = 0; g2 < kG; ++g2) st[g2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int r = kb * 16 + (lane & 15);
 #pragma unroll
       for (int ks = 0; ks < kMlaKSteps; ++ks) {
         const bf16x8 kf = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const uint4*>(&tile[tile_off(r, ks * 4 + grp)]));
-#pragma unroll
-        for (int g2 = 0; g2 < kG; ++g2)
-          st[g2][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g2][ks], st[g2][kb], 0, 0, 0);
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[kb], 0, 0, 0);
       }
     }
 
-    // ---- online softmax; this lane: one head per group, keys 16*kb + 4*grp + i
-    bf16x8 pb[kG][2];
-#pragma unroll
-    for (int g2 = 0; g2 < kG; ++g2) {
+    // ---- online softmax; this lane: head h, keys 16*kb + 4*grp + i
+    bf16x8 pb[2];
+    {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kb * 16 + grp * 4 + i;
-          float l = st[g2][kb][i] * scale2;
-          if constexpr (kFp8) l *= kscale[key];
+          float l = st[kb][i] * scale2 * kscale[key];
           l = rows[key] >= 0 ? l : -INFINITY;
-          st[g2][kb][i] = l;
+          st[kb][i] = l;
           mx = fmaxf(mx, l);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // move the reference only when needed (uniform over the wave)
-      const bool need = mx > m_ref[g2] + kRescaleLog2;
+      const bool need = mx > m_ref + kRescaleLog2;
       if (__ballot(need)) {
-        const float m_new = need ? mx : m_ref[g2];
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[g2] - m_new);   // 0 when m_ref = -inf
-        l_run[g2] *= alpha;
+        const float m_new = need ? mx : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 when m_ref = -inf
+        l_run *= alpha;
 #pragma unroll
-        for (int cb = 0; cb < kMlaCBlocks; ++cb) o[g2][cb] *= alpha;
-        m_ref[g2] = m_new;
+        for (int cb = 0; cb < kMlaCBlocks; ++cb) o[cb] *= alpha;
+        m_ref = m_new;
       }
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float p = __builtin_amdgcn_exp2f(st[g2][kb][i] - m_ref[g2]);
+          float p = __builtin_amdgcn_exp2f(st[kb][i] - m_ref);
           psum += p;
-          if constexpr (kFp8) p *= kscale[kb * 16 + grp * 4 + i];   // fold row scale into P
-          pb[g2][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(p);
+          p *= kscale[kb * 16 + grp * 4 + i];   // fold the row scale into P
+          pb[kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(p);
         }
       psum += __shfl_xor(psum, 16);
       psum += __shfl_xor(psum, 32);
-      l_run[g2] += psum;
+      l_run += psum;
     }
 
-    // ---- O^T += V^T P^T, two steps of 32 keys; one V fragment feeds both
-    //      head groups
+    // ---- O^T += V^T P^T, two steps of 32 keys
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
       const int r0 = (2 * kp) * 16 + grp * 4;       // keys r0..r0+3
       const int r1 = (2 * kp + 1) * 16 + grp * 4;   // keys r1..r1+3
 #pragma unroll
       for (int cb = 0; cb < kMlaCBlocks; ++cb) {
-        bf16x8 vf;
-        if constexpr (kTrV) {
-          // ds_read_b64_tr_b16: in each 16-lane group, lane i names 4
-          // consecutive bf16 of row (base + i/4), columns 4*(i%4)..+3 of
-          // the 16-column block; lane i receives column i of the 4 rows.
-          const int li = lane & 15;
-          const int chunk = 2 * cb + ((li & 3) >> 1);
-          const int sub = (li & 1) * 8;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(&tile[tile_off(r0 + (li >> 2), chunk) + sub]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(&tile[tile_off(r1 + (li >> 2), chunk) + sub]));
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          vf = __builtin_bit_cast(bf16x8, both);
-        } else {
-          const int c = cb * 16 + (lane & 15);        // value column
-          const int chunk = c >> 3;
-          const int within = (c & 7) * 2;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vf[i] = *reinterpret_cast<const __bf16*>(&tile[tile_off(r0 + i, chunk) + within]);
-            vf[4 + i] = *reinterpret_cast<const __bf16*>(&tile[tile_off(r1 + i, chunk) + within]);
-          }
-        }
-#pragma unroll
-        for (int g2 = 0; g2 < kG; ++g2)
-          o[g2][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[g2][kp], o[g2][cb], 0, 0, 0);
+        // ds_read_b64_tr_b16: in each 16-lane group, lane i names 4
+        // consecutive bf16 of row (base + i/4), columns 4*(i%4)..+3 of the
+        // 16-column block; lane i receives column i of the 4 rows.
+        const int li = lane & 15;
+        const int chunk = 2 * cb + ((li & 3) >> 1);
+        const int sub = (li & 1) * 8;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(&tile[tile_off(r0 + (li >> 2), chunk) + sub]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(&tile[tile_off(r1 + (li >> 2), chunk) + sub]));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[kp], o[cb], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 
   // ---- epilogue
-#pragma unroll
-  for (int g2 = 0; g2 < kG; ++g2) {
-    const int h = hbase + 16 * g2;
-    if (a.n_splits == 1) {
-      const float inv = l_run[g2] > 0.f ? 1.f / l_run[g2] : 0.f;
-      const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + grp * 4;
-      if (a.out_dtype == DS_BF16) {
-        uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
-#pragma unroll
-        for (int cb = 0; cb < kMlaCBlocks; ++cb) {
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(o[g2][cb][0] * inv) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(o[g2][cb][1] * inv)) << 16);
-          pk.y = f32_to_bf16_bits(o[g2][cb][2] * inv) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(o[g2][cb][3] * inv)) << 16);
-          *reinterpret_cast<uint2*>(out + cb * 16) = pk;
-        }
-      } else {
-        float* out = static_cast<float*>(a.out) + obase;
-#pragma unroll
-        for (int cb = 0; cb < kMlaCBlocks; ++cb)
-          *reinterpret_cast<float4*>(out + cb * 16) =
-              make_float4(o[g2][cb][0] * inv, o[g2][cb][1] * inv, o[g2][cb][2] * inv,
-                          o[g2][cb][3] * inv);
-      }
-      if (a.lse && grp == 0)
-        a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
-            l_run[g2] > 0.f ? (m_ref[g2] + log2f(l_run[g2])) * kLn2 : -INFINITY;
-    } else {
-      uint16_t* po = mla_partial_o(a, j, split, h) + grp * 4;
+  if (a.n_splits == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + grp * 4;
+    if (a.out_dtype == DS_BF16) {
+      uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
 #pragma unroll
       for (int cb = 0; cb < kMlaCBlocks; ++cb)
-        mla_store_bf16x4(po + cb * 16, o[g2][cb][0], o[g2][cb][1], o[g2][cb][2], o[g2][cb][3]);
-      if (grp == 0) {
-        float* pml = mla_partial_ml(a, j, split, h);
-        pml[0] = m_ref[g2];
-        pml[1] = l_run[g2];
-      }
+        mla_store_bf16x4(out + cb * 16, o[cb][0] * inv, o[cb][1] * inv, o[cb][2] * inv, o[cb][3] * inv);
+    } else {
+      float* out = static_cast<float*>(a.out) + obase;
+#pragma unroll
+      for (int cb = 0; cb < kMlaCBlocks; ++cb)
+        *reinterpret_cast<float4*>(out + cb * 16) =
+            make_float4(o[cb][0] * inv, o[cb][1] * inv, o[cb][2] * inv, o[cb][3] * inv);
+    }
+    if (a.lse && grp == 0)
+      a.lse[static_cast<int64_t>(j) * a.n_heads + h] =
+          l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : -INFINITY;
+  } else {
+    uint16_t* po = mla_partial_o(a, j, split, h) + grp * 4;
+#pragma unroll
+    for (int cb = 0; cb < kMlaCBlocks; ++cb)
+      mla_store_bf16x4(po + cb * 16, o[cb][0], o[cb][1], o[cb][2], o[cb][3]);
+    if (grp == 0) {
+      float* pml = mla_partial_ml(a, j, split, h);
+      pml[0] = m_ref;
+      pml[1] = l_run;
     }
   }
 }
 
-// ------------------------------------------------- bf16 KV, pipelined
-// One workgroup of 2*kG waves (kG = n_heads/32) per (query, split of its
-// rows), in two groups of kG waves; group g owns heads [g*H/2, (g+1)*H/2).
-//   * QK + softmax: wave wg of group g owns 16 heads, g*H/2 + 16*wg + 0..15.
-//     S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K from LDS and Q^T (72
-//     VGPRs) in registers; the online softmax of a head lives in the lane
-//     group that owns it.  The bf16 softmax weights P go to LDS.
-//   * PV: wave wg owns output columns [wg*512/kG, (wg+1)*512/kG) of its
-//     group's heads: O^T[c, h] += V^T[c, key] P^T[key, h], so each V
-//     fragment (LDS transpose read) feeds kG MFMAs.  O^T is 128 fp32
-//     registers per lane.
-//   * Ping-pong: group 1 runs one phase behind group 0 (an extra barrier
-//     before its loop), so while one group does QK + softmax of tile t (LDS
-//     reads of K, exp on the vector ALU) the other does PV of its previous
-//     tile (MFMA-dense) on the same SIMDs.  Each tile lives in LDS for three
-//     phases, so tiles are triple-buffered.
-// 32-row tiles are gathered straight into LDS (global_load_lds_dwordx4, no
-// VGPRs) by group 0 during its PV phase, two tiles ahead.
-// Lazy rescaling: a head's reference max moves only when a tile raises it
-// by more than 2^kRescaleLog2; the owner publishes the factor and every
-// wave of the group rescales its columns of that head.
+// ------------------------------------------- tiles of the bf16 kernel
 constexpr int kPipeTile = 32;                                     // rows per tile
-// Padded LDS row of the pipelined kernel: 1184 bytes (74 chunks).  With
-// this stride both the K-fragment reads (16 rows, one chunk) and the V
-// transpose reads (4 rows x 32 bytes per 16-lane group) are free of bank
-// conflicts (measured: 1152 is 4x and 1168 1.5x slower for one of them),
-// and a 32-row tile is exactly 37 DMA wave-instructions.
-constexpr int kPipeRow = kMlaRowBytes + 32;
-constexpr int kDmaRowChunks = kPipeRow / 16;                      // 74 (72 + pad)
-constexpr int kPipeTileChunks = kPipeTile * kDmaRowChunks;        // 2368
-constexpr int kPipeTileInst = kPipeTileChunks / kWave;            // 37
 constexpr int kMlaMaxKeys = 2048;
 
 // Three tile buffers.  The gathers into them are issued as instructions the
-// compiler does not see (mla_gather_issue), so it inserts no wait for them
+// compiler does not see (wide_gather_issue), so it inserts no wait for them
 // before reading a buffer; the kernel waits for its gathers itself (vmcnt
-// before the barrier that opens a tile).
-constexpr int kPipeTileBytes = kPipeTile * kPipeRow;              // 37888
+// before the barrier that opens a tile).  A buffer holds one 36 KB tile;
+// the stride leaves 1 KB between buffers.
+constexpr int kPipeTileBytes = kPipeTile * (kMlaRowBytes + 32);   // 37888
 __shared__ __align__(16) uint8_t g_mla_bufs[3 * kPipeTileBytes];
 
 // s_waitcnt immediate that waits until at most n vector-memory operations
 // of this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
-
-// DMA wave-instructions per wave and tile when kW waves share a tile's
-// gather (every wave issues the same count; slots past the last
-// instruction repeat the wave's previous one: identical bytes to the same
-// place).
-template <int kW>
-struct MlaIssue {
-  static constexpr int kPer = (kPipeTileInst + kW - 1) / kW;
-};
-constexpr int kMlaIssueMax = kPipeTileInst;
-
-template <int kW>
-__device__ __forceinline__ int mla_gather_inst(int wave, int i) {
-  const int m = wave + i * kW;
-  return m < kPipeTileInst ? m : m - kW;
-}
 
 // Cross-lane reductions over the four 16-lane rows of a wave (lanes l,
 // l^16, l^32, l^48) with the row-swap permutes: no LDS round trip.
@@ -483,396 +384,6 @@ __device__ __forceinline__ float mla_rows_sum(float v) {
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// One DMA wave-instruction of a tile gather: instruction m fills LDS
-// chunks [64m, 64m+64); lane l's chunk is row (64m+l)/74, column
-// (64m+l)%74 (columns 72, 73 are padding and re-read column 71).  Empty
-// slots (-1) read row 0: their logits are masked and their softmax weight
-// is 0.  The lane id is made opaque so this per-lane arithmetic is
-// recomputed at every call instead of being hoisted out of the tile loop:
-// hoisted values get spilled, and a scratch reload between two DMA
-// instructions would wait for the earlier gather (vmcnt counts both).
-__device__ __forceinline__ int mla_gather_row(int m, int lane) {
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
-  return (m * kWave + ln) / kDmaRowChunks;
-}
-
-__device__ __forceinline__ void mla_gather_issue(const uint8_t* kv, uint8_t* buf, int m, int lane,
-                                                 int32_t row) {
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
-  const int P = m * kWave + ln;
-  const int c = P - (P / kDmaRowChunks) * kDmaRowChunks;
-  const int cc = c < kMlaRowChunks ? c : kMlaRowChunks - 1;
-  row = row < 0 ? 0 : row;
-  const uint8_t* src = kv + static_cast<int64_t>(row) * kMlaRowBytes + cc * 16;
-  // LDS destination of lane l: M0 + 16*l (M0 = this instruction's chunk
-  // block, the same for the whole wave); one wait state between writing M0
-  // and the instruction that reads it
-  const uint32_t dst = static_cast<uint32_t>(
-      (size_t)((__attribute__((address_space(3))) uint8_t*)(buf + m * kWave * 16)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(dst))
-               : "memory", "m0");
-}
-
-// This wave's slots of the gather of tile rows sidx[t0 .. t0+31] into buf
-// (row indices read first: one LDS round trip).
-template <int kW>
-__device__ __forceinline__ void mla_issue_tile(const uint8_t* kv, uint8_t* buf, const int32_t* sidx,
-                                               int t0, int wave, int lane) {
-  constexpr int kPer = MlaIssue<kW>::kPer;
-  int32_t row[kMlaIssueMax];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) row[i] = sidx[t0 + mla_gather_row(mla_gather_inst<kW>(wave, i), lane)];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) mla_gather_issue(kv, buf, mla_gather_inst<kW>(wave, i), lane, row[i]);
-}
-
-template <int kG>
-struct MlaShared {
-  static constexpr int kHeads = 32 * kG;
-  static constexpr int kHalf = 16 * kG;   // heads per group
-  uint4 qrope[2][4][kHeads];   // rope k-steps of Q^T: [ks-16][lane group][head]
-  int32_t sidx[kMlaMaxKeys];
-  uint4 p[2][4][kHalf];        // P^T fragments: [group][lane group][head in group]
-  float alpha[2][kHalf];       // per-tile rescale factor of each head
-  int32_t rescale[2][kG];      // wave wg of group g raised a reference max
-  int32_t wave_cnt[2 * kG];    // index compaction scratch
-  float m_fin[kHeads], l_fin[kHeads];
-};
-
-template <bool kTrV, int kG>
-__global__ void __launch_bounds__(kWave * 2 * kG)
-mla_bf16_pipelined_kernel(MlaArgs a, int32_t keys_per_split) {
-  constexpr int kW = 2 * kG;
-  constexpr int kThreads = kWave * kW;
-  constexpr int kHalf = 16 * kG;              // heads per group
-  constexpr int kCols = kMlaDl / kG;          // output columns per wave
-  constexpr int kCB = kCols / 16;             // 16-column blocks per wave
-  constexpr int kCBC = kCB < 4 ? kCB : 4;     // column blocks per PV chunk
-  constexpr int kPer = MlaIssue<kW>::kPer;    // DMA wave-instructions per wave and tile
-  __shared__ MlaShared<kG> sh;
-
-  const int32_t j = blockIdx.x / a.n_splits;
-  const int32_t split = blockIdx.x - j * a.n_splits;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = wave / kG;                    // group
-  const int wg = wave - g * kG;               // wave within the group
-  const int grp = lane >> 4;
-  const int li = lane & 15;
-  const int hq = wg * 16 + li;                // head (within the group) this lane keeps
-  const int h_own = g * kHalf + hq;
-
-  const int32_t s_begin = split * keys_per_split;
-  int32_t s_end = s_begin + keys_per_split;
-  s_end = s_end < a.topk ? s_end : a.topk;
-  const int32_t n_keys = s_end > s_begin ? s_end - s_begin : 0;
-  // Stage the split's valid row indices in LDS, compacted to the front in
-  // their given order (ordered ballot scan), so empty slots cost no tiles.
-  const int32_t* idx_row = a.topk_idx + static_cast<int64_t>(j) * a.topk + s_begin;
-  int32_t n_valid = 0;
-  for (int32_t i0 = 0; i0 < n_keys; i0 += kThreads) {
-    const int32_t i = i0 + tid;
-    const int32_t r = i < n_keys ? idx_row[i] : -1;
-    const bool ok = r >= 0 && r < a.kv_rows;
-    const uint64_t ball = __ballot(ok);
-    if (lane == 0) sh.wave_cnt[wave] = static_cast<int32_t>(__popcll(ball));
-    __syncthreads();
-    int32_t before = n_valid, total = 0;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) {
-      const int32_t c = sh.wave_cnt[w];
-      before += w < wave ? c : 0;
-      total += c;
-    }
-    if (ok) sh.sidx[before + __popcll(ball & ((1ull << lane) - 1ull))] = r;
-    n_valid += total;
-    __syncthreads();
-  }
-  const int32_t n_tiles = static_cast<int32_t>(ceil_div(n_valid, kPipeTile));
-  for (int32_t i = n_valid + tid; i < n_tiles * kPipeTile; i += kThreads) sh.sidx[i] = -1;
-
-  // Q^T fragments (B operand of QK): head h_own, dims 32*ks + 8*grp + 0..7;
-  // the 16 latent k-steps stay in VGPRs, the 2 rope k-steps in LDS (this
-  // keeps the wave clear of register spills, whose scratch reloads would
-  // also wait on the in-flight tile gathers)
-  constexpr int kQReg = kMlaDl / 32;   // 16
-  bf16x8 qf[kQReg];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        (static_cast<int64_t>(j) * a.n_heads + h_own) * kMlaD + grp * 8;
-#pragma unroll
-    for (int ks = 0; ks < kQReg; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + ks * 32));
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      sh.qrope[r][grp][h_own] = *reinterpret_cast<const uint4*>(q + (kQReg + r) * 32);
-  }
-  // O^T[c, h]: column block cb of this wave, head block hg of the group
-  // (head g*H/2 + hg*16 + li, columns 16*cb + 4*grp + 0..3 of this wave's
-  // range)
-  f32x4 o[kCB][kG];
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-    for (int hg = 0; hg < kG; ++hg) o[cb][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_run = 0.f;
-  const float scale2 = a.sm_scale * kLog2e;
-  const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
-  // Q loads complete here, before any gather is in flight: a wait for them
-  // inside the tile loop would also wait for the gathers
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  __syncthreads();   // sidx and rope ready
-  // Gathers: every wave issues its slots of tile t+2 while tile t is in
-  // use (group 0 during its PV(t), group 1 during its QK(t); both into the
-  // buffer of tile t-1, which both groups have finished with by then), and
-  // waits for its slots of a tile before the barrier after which group 0
-  // opens it (group 0: the tile-opening barrier; group 1, one phase
-  // behind: the P barrier of the step before).  Here: tiles 0 and 1.
-  if (n_tiles > 0) mla_issue_tile<kW>(kv, g_mla_bufs, sh.sidx, 0, wave, lane);
-  if (n_tiles > 1) mla_issue_tile<kW>(kv, g_mla_bufs + kPipeTileBytes, sh.sidx, kPipeTile, wave, lane);
-  if (g == 1) {
-    // group 1 runs one phase behind; its part of tile 0 lands before
-    // group 0 opens it
-    if (n_tiles > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  }
-
-  // tile t lives in buffer t mod 3
-  for (int32_t t = 0, b = 0; t < n_tiles; ++t, b = b == 2 ? 0 : b + 1) {
-    // this wave's gather of tile t landed (tile t+1 may still be in flight)
-    if (g == 0) {
-      // group 0's slots of tile t landed (those of tile t+1 may be in flight)
-      if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();         // tile t complete for every wave
-    asm volatile("" ::: "memory");
-    // QK and softmax are this SIMD's critical path: issue ahead of the
-    // other group's PV products
-    __builtin_amdgcn_s_setprio(2);
-    // tile t+2 goes into the buffer of tile t-1
-    const bool gather = t + 2 < n_tiles;
-    uint8_t* gbuf = g_mla_bufs + (b == 0 ? 2 : b - 1) * kPipeTileBytes;
-    const int t0g = (t + 2) * kPipeTile;
-    // row index of this wave's next gather slot, read one slot ahead
-    int32_t grow = (g == 1 && gather) ? sh.sidx[t0g + mla_gather_row(mla_gather_inst<kW>(wave, 0), lane)] : 0;
-    const uint8_t* tile = g_mla_bufs + b * kPipeTileBytes;
-    // per-lane offsets recomputed every tile from an opaque copy of the lane
-    // id: hoisted out of the loop they would be spilled
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int li_t = ln & 15, grp_t = ln >> 4;
-    const int32_t my_row = lane < kPipeTile ? sh.sidx[t * kPipeTile + lane] : -1;
-    const uint64_t valid = __ballot(my_row >= 0);
-
-    // ---- S^T = K Q^T for this wave's 16 heads: 2 blocks of 16 keys; the
-    //      fragments of k-step ks+1 are read while ks is multiplied
-    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const int koff = li_t * kPipeRow + grp_t * 16;
-    auto kfrag = [&](int kb, int ks) {
-      return __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(tile + koff + kb * 16 * kPipeRow + ks * 64));
-    };
-    bf16x8 k0 = kfrag(0, 0), k1 = kfrag(1, 0);
-#pragma unroll
-    for (int ks = 0; ks < kMlaKSteps; ++ks) {
-      bf16x8 n0 = k0, n1 = k1;
-      if (ks + 1 < kMlaKSteps) {
-        n0 = kfrag(0, ks + 1);
-        n1 = kfrag(1, ks + 1);
-      }
-      const bf16x8 qv = ks < kQReg ? qf[ks < kQReg ? ks : 0]
-                                   : __builtin_bit_cast(bf16x8, sh.qrope[ks - kQReg][grp][h_own]);
-      st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv, st[0], 0, 0, 0);
-      st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv, st[1], 0, 0, 0);
-      k0 = n0;
-      k1 = n1;
-      // group 1: this wave's gather slots of tile t+2, spread over the k-steps
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if (i * kMlaKSteps / kPer == ks && g == 1 && gather) {
-          mla_gather_issue(kv, gbuf, mla_gather_inst<kW>(wave, i), lane, grow);
-          if (i + 1 < kPer) grow = sh.sidx[t0g + mla_gather_row(mla_gather_inst<kW>(wave, i + 1), lane)];
-        }
-      }
-    }
-    // ---- online softmax of head h_own over keys 16*kb + 4*grp + i
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb * 16 + grp * 4 + i;
-        const float l = ((valid >> key) & 1ull) ? st[kb][i] * scale2 : -INFINITY;
-        st[kb][i] = l;
-        mx = fmaxf(mx, l);
-      }
-    mx = mla_rows_max(mx);
-    const bool need = mx > m_ref + kRescaleLog2;
-    float alpha = 1.f;
-    if (need) {
-      alpha = __builtin_amdgcn_exp2f(m_ref - mx);   // 0 on the first raise (m_ref = -inf)
-      m_ref = mx;
-      l_run *= alpha;
-    }
-    const bool wave_rescales = __ballot(need) != 0ull;
-    if (lane < 16) sh.alpha[g][hq] = alpha;
-    if (lane == 0) sh.rescale[g][wg] = wave_rescales;
-    float psum = 0.f;
-    bf16x8 pv;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pw = valid ? __builtin_amdgcn_exp2f(st[kb][i] - m_ref) : 0.f;
-        psum += pw;
-        pv[kb * 4 + i] = static_cast<__bf16>(pw);
-      }
-    psum = mla_rows_sum(psum);
-    l_run += psum;
-    sh.p[g][grp][hq] = __builtin_bit_cast(uint4, pv);
-    // P and the rescale factors of the group visible to all its waves.
-    // Only LDS traffic is waited for: a fenced barrier would also wait for
-    // the tile gathers in flight.
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    if (g == 1) {
-      // group 1's slots of tile t+1 landed before group 0 opens it after
-      // this barrier (those of tile t+2 may be in flight)
-      if (gather) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPer));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_setprio(0);
-    // group 0: its gather slots of tile t+2 go out spread over the products
-    if (g == 0 && gather) grow = sh.sidx[t0g + mla_gather_row(mla_gather_inst<kW>(wave, 0), lane)];
-
-    // ---- rescale this wave's columns of any head whose reference moved
-    bool any = false;
-#pragma unroll
-    for (int w = 0; w < kG; ++w) any |= sh.rescale[g][w] != 0;
-    if (any) {
-#pragma unroll
-      for (int hg = 0; hg < kG; ++hg) {
-        const float al = sh.alpha[g][hg * 16 + li];
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) o[cb][hg] *= al;
-      }
-    }
-    // ---- O^T += V^T P^T for this wave's column blocks, the group's heads
-    const int voff = (4 * grp_t + (li_t >> 2)) * kPipeRow + ((li_t & 3) >> 1) * 16 +
-                     (li_t & 1) * 8 + wg * kCols * 2;
-    // column blocks in chunks of kCBC: the chunk's V^T fragments stay in
-    // registers while every head block of P multiplies them
-#pragma unroll
-    for (int c0 = 0; c0 < kCB; c0 += kCBC) {
-      bf16x8 vf[kCBC];
-#pragma unroll
-      for (int c = 0; c < kCBC; ++c) {
-        const int cb = c0 + c;
-        if constexpr (kTrV) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(tile + voff + cb * 32));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(tile + voff + 16 * kPipeRow + cb * 32));
-          vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        } else {
-          const int col = wg * kCols + cb * 16 + li;
-          const uint8_t* p0 = tile + 4 * grp * kPipeRow + (col >> 3) * 16 + (col & 7) * 2;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vf[c][i] = *reinterpret_cast<const __bf16*>(p0 + i * kPipeRow);
-            vf[c][4 + i] = *reinterpret_cast<const __bf16*>(p0 + (16 + i) * kPipeRow);
-          }
-        }
-      }
-      bf16x8 pf = __builtin_bit_cast(bf16x8, sh.p[g][grp][li]);
-#pragma unroll
-      for (int hg = 0; hg < kG; ++hg) {
-        bf16x8 pn = pf;
-        if (hg + 1 < kG) pn = __builtin_bit_cast(bf16x8, sh.p[g][grp][(hg + 1) * 16 + li]);
-#pragma unroll
-        for (int c = 0; c < kCBC; ++c) {
-          o[c0 + c][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c], pf, o[c0 + c][hg], 0, 0, 0);
-          const int prod = c0 * kG + hg * kCBC + c;
-#pragma unroll
-          for (int i = 0; i < kPer; ++i) {
-            if (i * kG * kCB / kPer == prod && g == 0 && gather) {
-              mla_gather_issue(kv, gbuf, mla_gather_inst<kW>(wave, i), lane, grow);
-              if (i + 1 < kPer)
-                grow = sh.sidx[t0g + mla_gather_row(mla_gather_inst<kW>(wave, i + 1), lane)];
-            }
-          }
-        }
-        pf = pn;
-      }
-    }
-  }
-  if (g == 0) __builtin_amdgcn_s_barrier();   // pairs with group 1's leading barrier
-
-  // ---- epilogue: owners publish (m, l); every wave writes its columns
-  if (lane < 16) {
-    sh.m_fin[h_own] = m_ref;
-    sh.l_fin[h_own] = l_run;
-  }
-  __syncthreads();
-  const int col0 = wg * kCols + grp * 4;
-#pragma unroll
-  for (int hg = 0; hg < kG; ++hg) {
-    const int h = g * kHalf + hg * 16 + li;
-    const float lf = sh.l_fin[h];
-    if (a.n_splits == 1) {
-      const float inv = lf > 0.f ? 1.f / lf : 0.f;
-      const int64_t obase = (static_cast<int64_t>(j) * a.n_heads + h) * kMlaDl + col0;
-      if (a.out_dtype == DS_BF16) {
-        uint16_t* out = static_cast<uint16_t*>(a.out) + obase;
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(o[cb][hg][0] * inv) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][1] * inv)) << 16);
-          pk.y = f32_to_bf16_bits(o[cb][hg][2] * inv) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(o[cb][hg][3] * inv)) << 16);
-          *reinterpret_cast<uint2*>(out + cb * 16) = pk;
-        }
-      } else {
-        float* out = static_cast<float*>(a.out) + obase;
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
-          *reinterpret_cast<float4*>(out + cb * 16) =
-              make_float4(o[cb][hg][0] * inv, o[cb][hg][1] * inv, o[cb][hg][2] * inv,
-                          o[cb][hg][3] * inv);
-      }
-    } else {
-      uint16_t* po = mla_partial_o(a, j, split, h) + col0;
-#pragma unroll
-      for (int cb = 0; cb < kCB; ++cb)
-        mla_store_bf16x4(po + cb * 16, o[cb][hg][0], o[cb][hg][1], o[cb][hg][2], o[cb][hg][3]);
-    }
-  }
-  if (lane < 16) {
-    if (a.n_splits == 1) {
-      if (a.lse)
-        a.lse[static_cast<int64_t>(j) * a.n_heads + h_own] =
-            l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : -INFINITY;
-    } else {
-      float* pml = mla_partial_ml(a, j, split, h_own);
-      pml[0] = m_ref;
-      pml[1] = l_run;
-    }
-  }
 }
 
 // Maxima as the bare instructions: the inputs are finite or -inf, and the
@@ -947,10 +458,6 @@ __device__ __forceinline__ void mla_qk_settle(f32x4& a, f32x4& b, f32x4& c, f32x
 // rows x 32 bytes) hit distinct banks.
 constexpr int kWideTileBytes = kPipeTile * kMlaRowBytes;         // 36864
 constexpr int kWideInst = kWideTileBytes / (kWave * 16);         // 36 blocks
-__device__ __forceinline__ int wide_off(int r, int x) {
-  const int hh = (x >> 4) & 1;
-  return (x >> 5) * 1024 + hh * 512 + (r ^ (hh << 3)) * 16 + (x & 15);
-}
 // per-lane byte offset of this lane's 16 bytes of K fragment (key block 0,
 // k-step 0); key block kb adds 256, k-step ks adds 2048
 __device__ __forceinline__ int wide_koff(int l) {
@@ -967,21 +474,31 @@ __device__ __forceinline__ int wide_voff(int l, int col0) {
 // tile row whose bytes lane l gathers
 __device__ __forceinline__ int wide_gather_slot(int l) { return (l & 31) ^ ((l >> 5) << 3); }
 
-// The global byte offset a lane gathers from for every DMA instruction of a
-// tile: its row (empty slots, -1, read row 0: their logits are masked and
-// their softmax weight is 0) and its half.  32-bit: the latent KV must be
-// smaller than 4 GiB.
-__device__ __forceinline__ uint32_t wide_gather_base(int32_t row, int l) {
-  row = row < 0 ? 0 : row;
-  return static_cast<uint32_t>(row) * kMlaRowBytes + static_cast<uint32_t>((l >> 5) << 4);
+// Keys of a tile that hold selected rows (valid rows are compacted to the
+// front, so only the last tile is partial): the first `rem` of 32.
+__device__ __forceinline__ uint64_t tile_valid_mask(int32_t rem) {
+  return rem >= kPipeTile ? 0xffffffffull : ((1ull << (rem > 0 ? rem : 0)) - 1ull);
 }
-// One DMA wave-instruction: block m of the tile at LDS address lds (the
-// block's start: lane l lands at lds + 16l) from bytes [32m, 32m+32) of the
-// lane's row.
-__device__ __forceinline__ void wide_gather_issue(const uint8_t* kv, uint32_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+
+// The global address a lane gathers from for the DMA instructions of a
+// tile: its row (a row of -1 reads row 0; the kernel pads with a selected
+// row instead), its half, and the issuing wave's first column block.
+// 64-bit per lane, so the latent KV may exceed 4 GiB; the blocks a wave
+// issues are kNW * 32 bytes apart.
+__device__ __forceinline__ const uint8_t* wide_gather_src(const uint8_t* kv, int32_t row, int l,
+                                                          int wave) {
+  row = row < 0 ? 0 : row;
+  return kv + static_cast<int64_t>(row) * kMlaRowBytes + ((l >> 5) << 4) + 32 * wave;
+}
+// One DMA wave-instruction: the block at LDS address lds (the block's
+// start: lane l lands at lds + 16l) from the lane's address src (bytes
+// [32m, 32m+32) of its row for block m).  The instruction's own offset
+// field stays 0: for loads into LDS it moves the LDS destination as well
+// as the global address, so the block offset is added to src instead.
+__device__ __forceinline__ void wide_gather_issue(const uint8_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(off), "s"(kv), "s"(lds)
+               : "v"(src), "s"(lds)
                : "memory", "m0");
 }
 
@@ -996,7 +513,7 @@ struct MlaWideShared {
   float m_fin[kHeads], l_fin[kHeads];
 };
 
-template <bool kTrV, int kNW, bool kLag>
+template <int kNW, bool kLag>
 __global__ void __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   constexpr int kThreads = kWave * kNW;
@@ -1086,7 +603,13 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
     lds_barrier();
   }
   const int32_t n_tiles = static_cast<int32_t>(ceil_div(n_valid, kPipeTile));
-  for (int32_t i = n_valid + tid; i < (n_tiles + 1) * kPipeTile; i += kThreads) sh.sidx[i] = -1;
+  // Slots past the valid rows (the last tile's tail, and the tile after it
+  // that the lagged loop gathers into a free buffer) repeat the last valid
+  // row: their logits are masked by position and their softmax weight is 0,
+  // but they must hold finite values (0 x NaN would poison PV), and a
+  // selected row is the one row the caller guarantees to be initialised.
+  const int32_t pad_row = n_valid > 0 ? sh.sidx[n_valid - 1] : 0;
+  for (int32_t i = n_valid + tid; i < (n_tiles + 1) * kPipeTile; i += kThreads) sh.sidx[i] = pad_row;
   if (tid < kNW) sh.bail[tid] = 0;
   const float scale2 = a.sm_scale * kLog2e;
   const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
@@ -1096,17 +619,16 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   auto slot_lds = [&](int b, int i) {
     return lds_bufs + static_cast<uint32_t>(b * kPipeTileBytes + (kNW * i + wave) * 1024);
   };
-  auto slot_off = [&](uint32_t base, int i) { return base + static_cast<uint32_t>(32 * (kNW * i + wave)); };
   auto row_of = [&](int t0) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    return wide_gather_base(sh.sidx[t0 + wide_gather_slot(ln)], ln);
+    return wide_gather_src(kv, sh.sidx[t0 + wide_gather_slot(ln)], ln, wave);
   };
   // all of this wave's slots of the tile with rows sidx[t0..] into buffer b
   auto issue_tile = [&](int b, int t0) {
-    const uint32_t base = row_of(t0);
+    const uint8_t* src = row_of(t0);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) wide_gather_issue(kv, slot_lds(b, i), slot_off(base, i));
+    for (int i = 0; i < kPer; ++i) wide_gather_issue(src + 32 * kNW * i, slot_lds(b, i));
   };
   // The first tile's gather goes out before the rope part of Q is loaded,
   // so that the two latencies overlap (the lagged loop issues it here on its
@@ -1129,7 +651,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   auto qk = [&](const uint8_t* tile, f32x4 (&st)[2][2], bool gather, int t0g, int gb) {
     // the gather's row is read first, so that waiting for it does not wait
     // for the K fragment reads behind it
-    const uint32_t gbase = gather ? row_of(t0g) : 0u;
+    const uint8_t* gsrc = gather ? row_of(t0g) : kv;
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int koff = wide_koff(ln);
@@ -1175,7 +697,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       }
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        if (i * kSpread / kPer == ks && gather) wide_gather_issue(kv, slot_lds(gb, i), slot_off(gbase, i));
+        if (i * kSpread / kPer == ks && gather) wide_gather_issue(gsrc + 32 * kNW * i, slot_lds(gb, i));
       }
     }
     mla_qk_settle(st[0][0], st[0][1], st[1][0], st[1][1]);
@@ -1243,20 +765,11 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
     if constexpr (kPV) {
 #pragma unroll
       for (int c = 0; c < kCBL; ++c) {
-        if constexpr (kTrV) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vtile + voff + c * 1024));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vtile + voff + 256 + c * 1024));
-          vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        } else {
-          const int x = (wave * kCols + c * 16 + li_t) * 2;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vf[c][i] = *reinterpret_cast<const __bf16*>(vtile + wide_off(4 * grp_t + i, x));
-            vf[c][4 + i] = *reinterpret_cast<const __bf16*>(vtile + wide_off(16 + 4 * grp_t + i, x));
-          }
-        }
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vtile + voff + c * 1024));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vtile + voff + 256 + c * 1024));
+        vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
       pf[0] = load_p(0);
     }
@@ -1290,7 +803,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
           nm[hb] = -m_ref[hb];
         }
       } else if constexpr (u == 5) {
-        beyond = (mx[0] > m_ref[0] + kWideBail) || (mx[1] > m_ref[1] + kWideBail);
+        beyond = !exact && ((mx[0] > m_ref[0] + kWideBail) || (mx[1] > m_ref[1] + kWideBail));
       } else if constexpr (u < 6 + 3 * 16) {       // weights exp2(scale2 * s - m_ref), three steps per value
         constexpr int v = (u - 6) / 3, ph = (u - 6) % 3;
         constexpr int hb = v >> 3, kb = (v >> 2) & 1, i = v & 3;
@@ -1340,7 +853,9 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  for (;;) {
+  // At most two passes: the second runs with the exact maximum, against
+  // which no tile can rise (its bail test is off), so the loop ends.
+  for (int pass = 0; pass < 2; ++pass) {
     if (exact) {
       // ---- first pass: exact maximum of every head over all rows (tiles
       //      gathered one at a time into buffer 0)
@@ -1350,8 +865,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
         issue_tile(0, t * kPipeTile);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __syncthreads();
-        const int32_t my_row = lane < kPipeTile ? sh.sidx[t * kPipeTile + lane] : -1;
-        const uint64_t valid = __ballot(my_row >= 0);
+        const uint64_t valid = tile_valid_mask(n_valid - t * kPipeTile);
         f32x4 st[2][2];
         qk(g_mla_bufs, st, false, 0, 0);
         float mx[2];
@@ -1451,10 +965,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       __builtin_amdgcn_s_barrier();       // tile t complete; tile t-1 consumed
       asm volatile("" ::: "memory");
       const uint8_t* tile = g_mla_bufs + b * kPipeTileBytes;
-      int lr = lane;
-      asm volatile("" : "+v"(lr));   // recomputed per tile, not kept (and spilled)
-      const int32_t my_row = lr < kPipeTile ? sh.sidx[t * kPipeTile + lr] : -1;
-      const uint64_t valid = __ballot(my_row >= 0);
+      const uint64_t valid = tile_valid_mask(n_valid - t * kPipeTile);
       // ---- QK, with the gather of tile t+2 into the buffer of tile t-1
       f32x4 st[2][2];
       qk(tile, st, t + 2 < n_tiles, (t + 2) * kPipeTile, b == 0 ? 2 : b - 1);
@@ -1465,7 +976,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         if (t == 0 && !exact) m_ref[hb] = mx[hb];
-        beyond |= mx[hb] > m_ref[hb] + kWideBail;
+        beyond |= !exact && mx[hb] > m_ref[hb] + kWideBail;
         float psum = 0.f;
         bf16x8 pv;
 #pragma unroll
@@ -1504,20 +1015,11 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
 #pragma unroll
         for (int c = 0; c < kCBC; ++c) {
           const int cb = c0 + c;
-          if constexpr (kTrV) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(tile + voff + cb * 1024));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(tile + voff + 256 + cb * 1024));
-            vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          } else {
-            const int x = (wave * kCols + cb * 16 + li) * 2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              vf[c][i] = *reinterpret_cast<const __bf16*>(tile + wide_off(4 * grp + i, x));
-              vf[c][4 + i] = *reinterpret_cast<const __bf16*>(tile + wide_off(16 + 4 * grp + i, x));
-            }
-          }
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tile + voff + cb * 1024));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tile + voff + 256 + cb * 1024));
+          vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
         bf16x8 pf = __builtin_bit_cast(bf16x8, sh.p[0][grp_t][li_t]);
 #pragma unroll
@@ -1693,27 +1195,16 @@ mla_combine_kernel(MlaArgs a) {
 }
 
 // ------------------------------------------------------------------ host
-// Value fragments are read with the LDS transpose instruction unless
-// DS32CP_MLA_SCALAR_V=1 selects the element-wise reads (same results; used
-// to cross-check the transpose layout).
-static bool mla_lag() {
-  const char* e = getenv("DS32CP_MLA_LAG");
-  return !(e && e[0] == '0');
-}
-static bool mla_transpose_reads() {
-  const char* e = getenv("DS32CP_MLA_SCALAR_V");
-  return !(e && e[0] == '1');
-}
-
 // fp8 rows -> bf16 rows of code * scale (round to nearest even), 16 codes
 // per thread: one 16-byte load, two 16-byte stores.
 __global__ void __launch_bounds__(256)
-widen_fp8_rows_kernel(const uint8_t* codes, const float* scale, int64_t rows, uint16_t* out) {
+widen_fp8_rows_kernel(const uint8_t* codes, const float* scale, int32_t scale_shift, int64_t rows,
+                      uint16_t* out) {
   constexpr int kPer = kMlaD / 16;   // 36 pieces of 16 codes per row
   const int64_t piece = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (piece >= rows * kPer) return;
   const int64_t r = piece / kPer;
-  const float sc = scale[r / kFp8BlockRows];
+  const float sc = scale[r >> scale_shift];
   const uint4 v = *reinterpret_cast<const uint4*>(codes + piece * 16);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[8];
@@ -1729,19 +1220,19 @@ widen_fp8_rows_kernel(const uint8_t* codes, const float* scale, int64_t rows, ui
   dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-ds_status launch_widen_fp8_rows(const void* codes, const float* scale, int64_t rows, void* out,
-                                hipStream_t s) {
+ds_status launch_widen_fp8_rows(const void* codes, const float* scale, int32_t scale_shift,
+                                int64_t rows, void* out, hipStream_t s) {
   if (rows <= 0) return DS_OK;
   const int64_t pieces = rows * (kMlaD / 16);
   widen_fp8_rows_kernel<<<static_cast<unsigned>(ceil_div(pieces, 256)), 256, 0, s>>>(
-      static_cast<const uint8_t*>(codes), scale, rows, static_cast<uint16_t*>(out));
+      static_cast<const uint8_t*>(codes), scale, scale_shift, rows, static_cast<uint16_t*>(out));
   return check_launch("sparse_mla (fp8 rows to bf16)");
 }
 
 int32_t mla_decode_splits(int32_t n_q, int32_t topk) {
-  // enough workgroups to cover the 256 CUs; at least 4 tiles per split
+  // enough workgroups to cover the compute units; at least 4 tiles per split
   const int32_t tiles = static_cast<int32_t>(ceil_div(topk, kMlaTile));
-  int32_t want = static_cast<int32_t>(ceil_div(256, n_q > 0 ? n_q : 1));
+  int32_t want = static_cast<int32_t>(ceil_div(device_cu_count(), n_q > 0 ? n_q : 1));
   int32_t max_splits = tiles / 4 > 0 ? tiles / 4 : 1;
   max_splits = max_splits < kMlaMaxSplits ? max_splits : kMlaMaxSplits;   // the combine's bound
   want = want < max_splits ? want : max_splits;
@@ -1767,54 +1258,14 @@ ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s) {
   const int32_t per_split =
       static_cast<int32_t>(round_up(ceil_div(a.topk, a.n_splits), kMlaTile));
   const int64_t blocks = static_cast<int64_t>(a.n_q) * a.n_splits;
-  const bool tr = mla_transpose_reads();
-  // the wide kernel addresses rows with 32-bit offsets
-  const bool wide = static_cast<uint64_t>(a.kv_rows) * kMlaRowBytes < (1ull << 32);
   if (a.kv_dtype == DS_BF16) {
-    if (!wide) switch (a.n_heads) {
-      case 32:
-        if (tr) mla_bf16_pipelined_kernel<true, 1><<<blocks, kWave * 2, 0, s>>>(a, per_split);
-        else mla_bf16_pipelined_kernel<false, 1><<<blocks, kWave * 2, 0, s>>>(a, per_split);
-        break;
-      case 64:
-        if (tr) mla_bf16_pipelined_kernel<true, 2><<<blocks, kWave * 4, 0, s>>>(a, per_split);
-        else mla_bf16_pipelined_kernel<false, 2><<<blocks, kWave * 4, 0, s>>>(a, per_split);
-        break;
-      default:
-        if (tr) mla_bf16_pipelined_kernel<true, 4><<<blocks, kWave * 8, 0, s>>>(a, per_split);
-        else mla_bf16_pipelined_kernel<false, 4><<<blocks, kWave * 8, 0, s>>>(a, per_split);
+    switch (a.n_heads) {
+      case 32: mla_bf16_wide_kernel<1, false><<<blocks, kWave * 1, 0, s>>>(a, per_split); break;
+      case 64: mla_bf16_wide_kernel<2, false><<<blocks, kWave * 2, 0, s>>>(a, per_split); break;
+      default: mla_bf16_wide_kernel<4, true><<<blocks, kWave * 4, 0, s>>>(a, per_split);
     }
-    else switch (a.n_heads) {
-      case 32:
-        if (tr) mla_bf16_wide_kernel<true, 1, false><<<blocks, kWave * 1, 0, s>>>(a, per_split);
-        else mla_bf16_wide_kernel<false, 1, false><<<blocks, kWave * 1, 0, s>>>(a, per_split);
-        break;
-      case 64:
-        if (tr) mla_bf16_wide_kernel<true, 2, false><<<blocks, kWave * 2, 0, s>>>(a, per_split);
-        else mla_bf16_wide_kernel<false, 2, false><<<blocks, kWave * 2, 0, s>>>(a, per_split);
-        break;
-      default:
-        if (mla_lag()) {
-          if (tr) mla_bf16_wide_kernel<true, 4, true><<<blocks, kWave * 4, 0, s>>>(a, per_split);
-          else mla_bf16_wide_kernel<false, 4, true><<<blocks, kWave * 4, 0, s>>>(a, per_split);
-        } else {
-          if (tr) mla_bf16_wide_kernel<true, 4, false><<<blocks, kWave * 4, 0, s>>>(a, per_split);
-          else mla_bf16_wide_kernel<false, 4, false><<<blocks, kWave * 4, 0, s>>>(a, per_split);
-        }
-    }
-    ds_status st = check_launch("sparse_mla");
-    if (st != DS_OK || a.n_splits == 1) return st;
-    dim3 cgrid(a.n_q, a.n_heads / kMlaCombineHeads);
-    mla_combine_kernel<<<cgrid, 256, 0, s>>>(a);
-    return check_launch("sparse_mla combine");
-  }
-  const int threads = kWave * (a.n_heads / (16 * kMlaGroups));
-  if (a.kv_dtype == DS_FP8_E4M3FN) {
-    if (tr) mla_mfma_kernel<true, true, kMlaGroups><<<blocks, threads, 0, s>>>(a, per_split);
-    else mla_mfma_kernel<true, false, kMlaGroups><<<blocks, threads, 0, s>>>(a, per_split);
-  } else {
-    if (tr) mla_mfma_kernel<false, true, kMlaGroups><<<blocks, threads, 0, s>>>(a, per_split);
-    else mla_mfma_kernel<false, false, kMlaGroups><<<blocks, threads, 0, s>>>(a, per_split);
+  } else {   // fp8 codes with per-row or per-block scales (decode)
+    mla_fp8_kernel<<<blocks, kWave * (a.n_heads / 16), 0, s>>>(a, per_split);
   }
   ds_status st = check_launch("sparse_mla");
   if (st != DS_OK || a.n_splits == 1) return st;

@@ -16,6 +16,8 @@
 // every key above the threshold and the lowest-position keys equal to it,
 // so the selected set is exactly the tie-to-lower-position set and the
 // output is deterministic.
+#include <mutex>
+
 #include "common.h"
 
 namespace ds32cp {
@@ -371,14 +373,17 @@ static void topk_set_smem() {
 
 ds_status launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.n_q == 0) return DS_OK;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the kernels' dynamic LDS limit, raised once per device (thread-safe)
+  static std::once_flag attr_once[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DS_ERR_HIP, "topk_select: no current HIP device");
+  std::call_once(attr_once[dev], [] {
     topk_set_smem<512, 0>();
     topk_set_smem<1024, 0>();
     topk_set_smem<512, 1>();
     topk_set_smem<1024, 2>();
-    attr_set = true;
-  }
+  });
   if (a.cand_score != nullptr) {
     // two phases: segments of kTopkSegLen positions (cached in LDS), then
     // the candidates of each row (n_seg * topk, cached in LDS)

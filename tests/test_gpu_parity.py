@@ -15,7 +15,8 @@ Gates (written out here, derived in the design doc):
 
 Small workloads are checked on every query row; the full-size ones (the
 launch configuration bench.py times) on sampled rows: the first and last
-four plus 24 seeded random rows.
+four, 24 seeded random rows, and the first and last local row of every
+request.
 """
 
 import numpy as np
@@ -37,11 +38,17 @@ SCORE_ATOL = 5e-5
 TOPK_BAND = 1e-3
 
 
-def _sample_rows(n, seed):
+def _sample_rows(n, seed, local_cu=None):
+    """First and last four rows, 24 seeded random rows, and the first and
+    last local row of every request (local_cu: the rank's request offsets)."""
     if n <= 64:
         return list(range(n))
     rng = np.random.default_rng(seed)
     pick = set(range(4)) | set(range(n - 4, n)) | set(rng.choice(n, 24, replace=False).tolist())
+    if local_cu is not None:
+        for lo, hi in zip(local_cu[:-1], local_cu[1:]):
+            if hi > lo:
+                pick |= {int(lo), int(hi) - 1}
     return sorted(pick)
 
 
@@ -129,7 +136,10 @@ def _check_prefill(name, all_rows):
     assert np.array_equal(g["kv_bytes"].reshape(T, -1), kv_bytes)
     ki_bytes = np.ascontiguousarray(inp["k_idx"]).view(np.uint8).reshape(T, -1)
     assert np.array_equal(g["ki_bytes"].reshape(T, -1), ki_bytes)
-    rows = list(range(n)) if all_rows else _sample_rows(n, wl.seed)
+    rows = list(range(n)) if all_rows else _sample_rows(n, wl.seed, om["local_cu"])
+    if not all_rows:   # every request's first and last local row is among them
+        for lo, hi in zip(om["local_cu"][:-1], om["local_cu"][1:]):
+            assert hi == lo or (lo in rows and hi - 1 in rows)
     gp.say(f"  oracle on {len(rows)} of {n} rows")
     sel = opl.indexer_topk_rows(rows, om, inp["q_idx"], wl.act_fmt, inp["w"], inp["k_idx"],
                                 wl.kv_fmt, inp["k_idx_scale"], wl.topk)
@@ -237,20 +247,6 @@ def test_mla_empty_and_out_of_range_rows():
         err = np.abs(out[j].float().cpu().numpy() - ro[0]).max()
         assert err <= 1e-2 * np.abs(ro[0]).max(), err
         assert np.abs(lse[j].cpu().numpy() - rl[0]).max() <= 1e-3
-
-
-def test_mla_transposed_value_reads_match_elementwise_reads(monkeypatch):
-    wl = get("small_prefill_3req_cp4")
-    n = 40
-    q = torch.randn(n, 128, 576, device=gp.DEV).bfloat16() / 24
-    kv = torch.randn(700, 576, device=gp.DEV).bfloat16() / 24
-    idx = torch.stack([torch.randperm(700, device=gp.DEV)[:256] for _ in range(n)]).int()
-    idx[5, 100:] = -1
-    a, la = ds.sparse_mla_prefill(q, kv, idx, wl.scale, 512)
-    monkeypatch.setenv("DS32CP_MLA_SCALAR_V", "1")
-    b, lb = ds.sparse_mla_prefill(q, kv, idx, wl.scale, 512)
-    torch.cuda.synchronize()
-    assert torch.equal(a, b) and torch.equal(la, lb)
 
 
 def test_decode_page_boundaries():

@@ -14,10 +14,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline():
     env = dict(os.environ)
     env.pop("WORLD_SIZE", None)
-    print("[bench contract] prefill_t8000_cp8, 2 steps", flush=True)
+    print("[bench contract] default workload (65536-token fp8 prefill), 2 steps", flush=True)
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2",
                         "--warmup", "1", "--settle-ms", "20", "--cpu-seconds", "0.5"],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=240)
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=400)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.strip()]
     assert len(lines) == 1, lines
@@ -31,7 +31,7 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline():
     # whole-step throughput: queries per step over the measured step time
     n = d["config"]["queries"]
     assert d["value"] == pytest.approx(n / (d["ms_per_step"] * 1e-3), rel=2e-3)
-    assert d["config"]["workload"] == "prefill_t8000_cp8"
+    assert d["config"]["workload"] == "prefill_t65536_cp8_fp8"
     roof = d["roofline"]
     assert roof["bound"] in ("hbm", "mfma", "alu")
     assert roof["unit"] in ("GB/s", "TFLOP/s")
