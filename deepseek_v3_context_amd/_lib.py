@@ -63,6 +63,9 @@ _SIGS = {
     "sparse_mla_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
     "sparse_mla_decode": ([_p, _i32, _p, _i32, _p, _i64, _p, _i32, _i32, _i32, _i32,
                            _i32, _f32, _p, _i32, _p, _p, _sz, _p], _i32),
+    "sparse_mla_decode_noalloc_scratch_bytes": ([], _sz),
+    "sparse_mla_decode_noalloc": ([_p, _i32, _p, _i32, _p, _i64, _p, _i32, _i32, _i32, _i32,
+                                   _i32, _f32, _p, _i32, _p, _p], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -314,6 +317,20 @@ def sparse_mla_decode(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale=
         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check("sparse_mla_decode", st)
+    return out, lse
+
+
+def sparse_mla_decode_noalloc(q, kv, topk_idx, sm_scale: float, d_latent: int, *, out,
+                              lse=None, kv_scale=None, stream=None):
+    """Step 5 (decode) with the library's own scratch for the split partials:
+    nothing is allocated, by this call or the library; the caller passes
+    every output buffer."""
+    n_q, H, d_qk = q.shape
+    st = lib.sparse_mla_decode_noalloc(
+        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv), _ptr(kv_scale), kv.shape[0],
+        _ptr(topk_idx), n_q, H, d_latent, d_qk - d_latent, topk_idx.shape[1], sm_scale, _ptr(out),
+        dtype_code(out), _ptr(lse), _stream(stream))
+    _check("sparse_mla_decode_noalloc", st)
     return out, lse
 
 

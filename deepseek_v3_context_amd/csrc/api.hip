@@ -3,6 +3,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -41,6 +42,33 @@ int32_t device_cu_count() {
 }
 
 static bool is_act_dtype(ds_dtype d) { return d == DS_F32 || d == DS_BF16; }
+
+// Library-owned scratch of the allocation-free decode entry point: the
+// split partials of sparse_mla_decode_noalloc.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code the array's
+// name is not a device address: its address on a device comes from
+// hipGetSymbolAddress (once per device, with that device current).
+constexpr size_t kNoAllocScratchBytes = 32u << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static ds_status scratch_ptr(void** out) {
+  static std::once_flag once[kMaxDevices];
+  static void* ptr[kMaxDevices] = {};
+  static hipError_t err[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DS_ERR_HIP, "sparse_mla_decode_noalloc: no current HIP device");
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    ptr[dev] = err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (ptr[dev] == nullptr)
+    return fail(DS_ERR_HIP, std::string("sparse_mla_decode_noalloc: hipGetSymbolAddress: ") +
+                                hipGetErrorString(err[dev]));
+  *out = ptr[dev];
+  return DS_OK;
+}
 
 }  // namespace ds32cp
 
@@ -343,6 +371,34 @@ ds_status sparse_mla_decode(const void* q, ds_dtype q_dtype, const void* kv,
   DS_REQUIRE(ws != nullptr && ws_bytes >= sparse_mla_workspace_size(n_q, n_heads, d_latent, topk),
              DS_ERR_WORKSPACE, "sparse_mla_decode: workspace smaller than sparse_mla_workspace_size()");
   if (q_dtype != DS_F32) a.n_splits = mla_decode_splits(n_q, topk);
+  return launch_sparse_mla(a, stream);
+}
+
+size_t sparse_mla_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+ds_status sparse_mla_decode_noalloc(const void* q, ds_dtype q_dtype, const void* kv,
+                                    ds_dtype kv_dtype, const float* kv_scale, int64_t kv_rows,
+                                    const int32_t* topk_idx, int32_t n_q, int32_t n_heads,
+                                    int32_t d_latent, int32_t d_rope, int32_t topk,
+                                    float sm_scale, void* out, ds_dtype out_dtype, float* lse,
+                                    hipStream_t stream) {
+  MlaArgs a{q, q_dtype, kv, kv_dtype, kv_scale, kv_rows, topk_idx, n_q, n_heads, d_latent,
+            d_rope, topk, sm_scale, out, out_dtype, lse, 1, nullptr};
+  ds_status st = check_mla("sparse_mla_decode_noalloc", a);
+  if (st != DS_OK) return st;
+  if (q_dtype == DS_F32 || n_q == 0) return launch_sparse_mla(a, stream);   // no partials
+  // the default split count when its partials fit the scratch, else the
+  // largest count that does (one split writes the output directly)
+  int32_t splits = mla_decode_splits(n_q, topk);
+  while (splits > 1 && mla_partials_bytes(n_q, n_heads, d_latent, splits) > kNoAllocScratchBytes)
+    --splits;
+  if (splits > 1) {
+    DS_REQUIRE(mla_partials_bytes(n_q, n_heads, d_latent, splits) <= kNoAllocScratchBytes,
+               DS_ERR_WORKSPACE, "sparse_mla_decode_noalloc: partials exceed the scratch");
+    st = scratch_ptr(&a.ws);
+    if (st != DS_OK) return st;
+  }
+  a.n_splits = splits;
   return launch_sparse_mla(a, stream);
 }
 

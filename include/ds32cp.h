@@ -28,7 +28,8 @@
  * - Pointers marked "dev" are device memory on the current HIP device;
  *   the caller owns them and keeps them alive until `stream` has finished
  *   the work.  The library allocates nothing, frees nothing and keeps no
- *   pointer after returning.
+ *   pointer after returning (sparse_mla_decode_noalloc's own scratch array,
+ *   a static device array of the library, aside).
  * - Calls are asynchronous on `stream` (NULL = the default stream) and never
  *   synchronise.
  * - Arrays are dense and row-major with the shapes given; indices are
@@ -260,6 +261,33 @@ ds_status sparse_mla_decode(const void* q, ds_dtype q_dtype, const void* kv,
                             int32_t d_rope, int32_t topk, float sm_scale,
                             void* out, ds_dtype out_dtype, float* lse,
                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Allocation-free variant of sparse_mla_decode, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments
+ * and results as sparse_mla_decode without ws/ws_bytes: the split partials
+ * live in a library-owned device array of
+ * sparse_mla_decode_noalloc_scratch_bytes() bytes (32 MiB), one per GPU,
+ * held until the process ends.  When the default split count's partials
+ * (n_q * splits * n_heads * 1 KB, plus their maxima and sums) would not fit,
+ * the call takes the largest split count that fits, down to one split,
+ * which needs no scratch; the results then differ from sparse_mla_decode's
+ * only by the bf16 rounding of fewer partials.  The call allocates nothing
+ * and never fails for size.  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads) race and give unspecified results; the array keeps the last
+ * call's contents, and nothing in it needs to start at zero.
+ * Errors: as sparse_mla_decode; DS_ERR_HIP if the array's device address
+ * cannot be obtained. */
+size_t sparse_mla_decode_noalloc_scratch_bytes(void);
+
+ds_status sparse_mla_decode_noalloc(const void* q, ds_dtype q_dtype, const void* kv,
+                                    ds_dtype kv_dtype, const float* kv_scale,
+                                    int64_t kv_rows, const int32_t* topk_idx,
+                                    int32_t n_q, int32_t n_heads, int32_t d_latent,
+                                    int32_t d_rope, int32_t topk, float sm_scale,
+                                    void* out, ds_dtype out_dtype, float* lse,
+                                    hipStream_t stream);
 
 /* ---------------------------------------------------------------------
  * Step D: the rank keeps its own tokens' KV in the paged cache pool.
