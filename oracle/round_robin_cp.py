@@ -187,6 +187,47 @@ def in_seq_split_ranges(num_tokens: int, cp_size: int) -> list[tuple[int, int]]:
     return out
 
 
+def in_seq_split_metadata(cu_seqlens, cp_size: int, cp_rank: int) -> dict:
+    """Contrast mode: per-rank metadata under the older contiguous split.
+
+    Section 4 part 1 of the blog post: each request is cut into ``cp_size``
+    consecutive chunks and rank ``r`` takes chunk ``r`` of every request (an
+    8000-token prompt on 8 ranks: rank 0 tokens 0..999, rank 1 1000..1999;
+    with a second, 800-token request rank 0 also takes its tokens 0..99).
+    Reading taken where the page is silent: a request of ``L`` tokens is
+    cut into chunks of ``ceil(L / cp_size)`` tokens (the last chunks may be
+    shorter or empty), at token granularity.
+
+    Written as plain enumeration: walk every token of every request, find
+    its chunk, keep it if the chunk is this rank's.  Same fields as
+    :func:`split_metadata`; ``kv_len`` is again position + 1 within the
+    request (causal).  Parity: pinned (tests/test_oracle_round_robin.py).
+    """
+    cu = [int(x) for x in np.asarray(cu_seqlens).tolist()]
+    if not cu or cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0 and be non-decreasing")
+    _check_rank(cp_size, cp_rank)
+    gids, batch_idx, kv_start, kv_len, local_cu = [], [], [], [], [0]
+    for b in range(len(cu) - 1):
+        length = cu[b + 1] - cu[b]
+        chunk = -(-length // cp_size)
+        for p in range(length):
+            if p // chunk == cp_rank:
+                gids.append(cu[b] + p)
+                batch_idx.append(b)
+                kv_start.append(cu[b])
+                kv_len.append(p + 1)
+        local_cu.append(len(gids))
+    as32 = lambda v: np.asarray(v, dtype=np.int32).reshape(-1)  # noqa: E731
+    return {
+        "global_idx": as32(gids),
+        "batch_idx": as32(batch_idx),
+        "local_cu": as32(local_cu),
+        "kv_start": as32(kv_start),
+        "kv_len": as32(kv_len),
+    }
+
+
 def _check_rank(cp_size: int, cp_rank: int) -> None:
     if cp_size < 1 or not (0 <= cp_rank < cp_size):
         raise ValueError(f"bad cp_size/cp_rank {cp_size}/{cp_rank}")

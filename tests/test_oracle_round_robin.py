@@ -159,3 +159,90 @@ def test_rerange_bytes_rows():
     x = rng.integers(0, 256, size=(77, 576), dtype=np.uint8)
     concat = rr.rank_concat(x, 8)
     assert np.array_equal(rr.rerange(concat, 77, 8, concat.shape[0] // 8), x)
+
+
+# ------------------------------------------------ in-sequence split (contrast)
+
+def test_in_seq_split_page_example_8000_tokens_on_8_ranks():
+    # section 4 part 1: rank r of 8 takes tokens 1000r .. 1000r + 999
+    g = _golden("cp8_8000tokens.json")
+    T, cp = g["num_tokens"], g["cp_size"]
+    for r, (lo, hi) in g["in_seq_split_printed_ranges"].items():
+        m = rr.in_seq_split_metadata([0, T], cp, int(r))
+        assert m["global_idx"].tolist() == list(range(lo, hi + 1))
+        assert m["local_cu"].tolist() == [0, hi - lo + 1]
+        assert m["kv_len"].tolist() == list(range(lo + 1, hi + 2))   # causal, inclusive
+    for r in range(cp):
+        assert rr.in_seq_split_metadata([0, T], cp, r)["global_idx"].size == g["tokens_per_rank"]
+
+
+def test_in_seq_split_page_two_request_example():
+    # same section: requests of 8000 and 800 tokens; rank 0 handles request
+    # A's tokens 0..999 and request B's tokens 0..99
+    g = _golden("cp8_8000tokens.json")
+    ex = g["two_request_example"]
+    cu = [0, ex["lengths"][0], ex["lengths"][0] + ex["lengths"][1]]
+    m = rr.in_seq_split_metadata(cu, g["cp_size"], 0)
+    (a_lo, a_hi), (b_lo, b_hi) = ex["rank0_ranges"]
+    want = list(range(a_lo, a_hi + 1)) + [cu[1] + p for p in range(b_lo, b_hi + 1)]
+    assert m["global_idx"].tolist() == want
+    assert m["batch_idx"].tolist() == [0] * (a_hi - a_lo + 1) + [1] * (b_hi - b_lo + 1)
+    assert m["kv_start"].tolist() == [0] * (a_hi - a_lo + 1) + [cu[1]] * (b_hi - b_lo + 1)
+    # the single-request ranges of the older helper agree with the metadata
+    for L in ex["lengths"]:
+        for r in range(g["cp_size"]):
+            lo, hi = rr.in_seq_split_ranges(L, g["cp_size"])[r]
+            got = rr.in_seq_split_metadata([0, L], g["cp_size"], r)["global_idx"].tolist()
+            assert got == list(range(lo, hi + 1))
+
+
+def test_in_seq_split_three_requests_worked_by_hand():
+    # lengths 8000, 800, 5 on 8 ranks (the page's imbalance example): chunks
+    # of 1000, 100 and 1 tokens; ranks 0..4 get one token of the 5-token
+    # request each, ranks 5..7 none; rank 6's tokens are A 6000..6999 and
+    # B 600..699.
+    cu = [0, 8000, 8800, 8805]
+    counts = [rr.in_seq_split_metadata(cu, 8, r)["global_idx"].size for r in range(8)]
+    assert counts == [1101] * 5 + [1100] * 3
+    m6 = rr.in_seq_split_metadata(cu, 8, 6)
+    assert m6["local_cu"].tolist() == [0, 1000, 1100, 1100]
+    assert m6["global_idx"].tolist() == list(range(6000, 7000)) + list(range(8600, 8700))
+    m4 = rr.in_seq_split_metadata(cu, 8, 4)
+    assert m4["global_idx"][-1] == 8804 and m4["kv_len"][-1] == 5
+
+
+def test_in_seq_split_causal_work_is_unbalanced():
+    # one 8000-token request on 8 ranks: rank r's causal pairs are
+    # sum_{p = 1000r}^{1000r + 999} (p + 1), from 500 500 (rank 0) to
+    # 7 500 500 (rank 7); round-robin gives every rank 3 996 000 - 4 004 000
+    for r in range(8):
+        m = rr.in_seq_split_metadata([0, 8000], 8, r)
+        lo, hi = 1000 * r, 1000 * r + 999
+        assert int(m["kv_len"].astype(np.int64).sum()) == (hi + 1) * (hi + 2) // 2 - lo * (lo + 1) // 2
+        rrm = rr.split_metadata([0, 8000], 8, r)
+        assert 3_996_000 <= int(rrm["kv_len"].astype(np.int64).sum()) <= 4_004_000
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_in_seq_split_partition_and_contiguity(seed):
+    rng = np.random.default_rng(100 + seed)
+    cu = _random_cu(rng, int(rng.integers(1, 7)), 60)
+    T = int(cu[-1])
+    for cp in (1, 2, 3, 8):
+        metas = [rr.in_seq_split_metadata(cu, cp, r) for r in range(cp)]
+        seen = np.concatenate([m["global_idx"] for m in metas]).astype(np.int64)
+        assert sorted(seen.tolist()) == list(range(T))          # each token exactly once
+        owner = np.empty(T, dtype=np.int64)
+        for r, m in enumerate(metas):
+            g = m["global_idx"].astype(np.int64)
+            owner[g] = r
+            assert np.array_equal(m["batch_idx"], np.searchsorted(cu, g, side="right") - 1)
+            assert np.array_equal(m["kv_start"], cu[m["batch_idx"]])
+            assert np.array_equal(m["kv_start"] + m["kv_len"] - 1, g)
+            per_req = np.diff(m["local_cu"])
+            assert np.array_equal(per_req, np.bincount(m["batch_idx"], minlength=len(cu) - 1))
+        # along each request the owning rank never decreases, and a rank's
+        # tokens of a request are consecutive (one chunk)
+        for b in range(len(cu) - 1):
+            o = owner[cu[b]: cu[b + 1]]
+            assert (np.diff(o) >= 0).all()
