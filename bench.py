@@ -52,7 +52,8 @@ def parse():
                          "long so that the GPU clocks have ramped (0 = off)")
     ap.add_argument("--all-ranks", action="store_true",
                     help="prefill: after the measurement, also time the step on every rank's "
-                         "share and report the per-rank spread (rank_balance)")
+                         "share under both split modes (round-robin, and the in-sequence split "
+                         "it replaces) and report the per-rank spread (rank_balance)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -96,12 +97,33 @@ def rank_max_kv_len(cu_seqlens, cp, r):
     return best
 
 
-def setup_prefill(wl, torch, ds, dev):
+def in_seq_max_kv_len(cu_seqlens, cp, r):
+    """Longest causal key range of rank r's queries under the in-sequence
+    split: per request of L tokens, its chunk r ends at min(L, (r+1) c),
+    c = ceil(L / cp)."""
+    best = 0
+    cu = [int(x) for x in cu_seqlens]
+    for lo, hi in zip(cu[:-1], cu[1:]):
+        L = hi - lo
+        c = -(-L // cp)
+        if L - r * c > 0:
+            best = max(best, min(L, (r + 1) * c))
+    return best
+
+
+def setup_prefill(wl, torch, ds, dev, split="round-robin"):
+    """Inputs and buffers of one rank's prefill step.  `split` picks the
+    rank's queries: round-robin (the method) or in-seq (the contiguous
+    split it replaces, for the per-rank balance contrast)."""
     import numpy as np
     from synth import draw_prefill
 
     T, cp, r = wl.num_tokens, wl.cp_size, wl.cp_rank
-    n = ds.cp_local_count(T, cp, r)
+    cu_host = wl.cu_seqlens()
+    if split == "in-seq":
+        n = ds.cp_in_seq_local_count(cu_host, cp, r)
+    else:
+        n = ds.cp_local_count(T, cp, r)
     inp = draw_prefill(wl, n)
 
     def up(arr, fmt):
@@ -129,7 +151,7 @@ def setup_prefill(wl, torch, ds, dev):
     del kv_l, ki_l
     st = {
         "n": n, "inp": inp, "cu": cu, "ids": ids, "kv_cat": kv_cat, "ki_cat": ki_cat,
-        "slot": slot,
+        "slot": slot, "split": split,
         "q_idx": up(inp["q_idx"], wl.act_fmt), "w": torch.from_numpy(inp["w"]).to(dev),
         "q": up(inp["q"], wl.act_fmt),
         "kv_scale": None if inp["kv_scale"] is None else torch.from_numpy(inp["kv_scale"]).to(dev),
@@ -144,7 +166,8 @@ def setup_prefill(wl, torch, ds, dev):
     st["ki"] = torch.empty((T, wl.d_idx), dtype=ki_cat.dtype, device=dev)
     # the longest causal range among the rank's queries (host-known from the
     # request lengths): it sizes the score rows and picks the top-k variant
-    st["max_len"] = rank_max_kv_len(inp["cu_seqlens"], cp, r)
+    st["max_len"] = (in_seq_max_kv_len if split == "in-seq" else rank_max_kv_len)(
+        inp["cu_seqlens"], cp, r)
     st["scores"] = torch.empty((n, ((st["max_len"] + 63) // 64) * 64), dtype=torch.float32,
                                device=dev)
     st["topk_idx"] = torch.empty((n, wl.topk), **i32)
@@ -158,7 +181,10 @@ def setup_prefill(wl, torch, ds, dev):
 def prefill_step(wl, ds, st, tm):
     T, cp, r = wl.num_tokens, wl.cp_size, wl.cp_rank
     m = st["meta"]
-    tm.run("cp_split_metadata", lambda: ds.cp_split_metadata(st["cu"], T, cp, r, rows_src=st["ids"], out=m))
+    if st.get("split") == "in-seq":
+        tm.run("cp_split_metadata", lambda: ds.cp_split_metadata_in_seq(st["cu"], T, cp, r, n_local=st["n"], rows_src=st["ids"], out=m))
+    else:
+        tm.run("cp_split_metadata", lambda: ds.cp_split_metadata(st["cu"], T, cp, r, rows_src=st["ids"], out=m))
     tm.run("kv_rerange(latent)", lambda: ds.kv_rerange(st["kv_cat"], st["slot"], T, cp, out=st["kv"]))
     tm.run("kv_rerange(indexer_k)", lambda: ds.kv_rerange(st["ki_cat"], st["slot"], T, cp, out=st["ki"]))
     tm.run("indexer_scores", lambda: ds.indexer_scores(st["q_idx"], st["w"], st["ki"], m["kv_start"], m["kv_len"], st["max_len"], k_scale=st["ki_scale"], scores=st["scores"]))
@@ -386,18 +412,21 @@ def cold_steps(wl, torch, ds, st, step, steps):
             "steps": steps, "flush": "512 MB device write before every step, outside the events"}
 
 
-def rank_balance(wl, torch, ds, dev, args):
-    """The step on every rank's share of the same prefill (round-robin
-    split), each rank set up on its own, warmed up and timed like the main
+def rank_balance(wl, torch, ds, dev, args, split):
+    """The step on every rank's share of the same prefill under one split
+    mode, each rank set up on its own, warmed up and timed like the main
     measurement (K steps between two device synchronisations, no events).
-    spread = (max - min) / mean of the per-rank step times."""
+    spread = (max - min) / mean of the per-rank step times.  The in-seq
+    step runs the same calls as the round-robin one (its rerange call
+    moves the same bytes as the in-seq mode's own would); only the split,
+    and so each rank's queries and causal ranges, differ."""
     import dataclasses
 
-    ms, nq = [], []
+    ms, nq, ipairs, mpairs = [], [], [], []
     for r in range(wl.cp_size):
-        print(f"[bench] rank balance: rank {r}", file=sys.stderr, flush=True)
+        print(f"[bench] rank balance ({split}): rank {r}", file=sys.stderr, flush=True)
         wr = dataclasses.replace(wl, cp_rank=r)
-        st = setup_prefill(wr, torch, ds, dev)
+        st = setup_prefill(wr, torch, ds, dev, split=split)
         none = Timed(torch, only=())
         t_end = time.perf_counter() + max(args.settle_ms, 0.0) * 1e-3
         for i in range(max(args.warmup, 1)):
@@ -412,11 +441,14 @@ def rank_balance(wl, torch, ds, dev, args):
         torch.cuda.synchronize()
         ms.append(round((time.perf_counter() - t0) / args.steps * 1e3, 4))
         nq.append(st["n"])
+        kl = st["meta"]["kv_len"].cpu().long()
+        ipairs.append(int(kl.sum()))
+        mpairs.append(int(kl.clamp(max=wl.topk).sum()))
         del st
         torch.cuda.empty_cache()
     mean = sum(ms) / len(ms)
-    return {"split": "round-robin", "ms_per_step": ms, "queries": nq,
-            "spread": round((max(ms) - min(ms)) / mean, 4)}
+    return {"split": split, "ms_per_step": ms, "queries": nq, "indexer_pairs": ipairs,
+            "mla_pairs": mpairs, "spread": round((max(ms) - min(ms)) / mean, 4)}
 
 
 def main():
@@ -529,7 +561,8 @@ def main():
     if wl.kind == "prefill":
         line["outside_step"] = own_kv_cache_write(wl, torch, ds, st, dev, args.steps)
         if args.all_ranks:
-            line["rank_balance"] = rank_balance(wl, torch, ds, dev, args)
+            line["rank_balance"] = {mode: rank_balance(wl, torch, ds, dev, args, mode)
+                                    for mode in ("round-robin", "in-seq")}
     if args.cpu_seconds > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, st, kv_len_host, args.cpu_seconds)

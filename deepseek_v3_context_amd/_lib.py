@@ -48,6 +48,10 @@ _SIGS = {
     "ds_cp_local_count": ([_i64, _i32, _i32], _i32),
     "cp_split_metadata": ([_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p,
                            _i64, _p], _i32),
+    "decode_metadata": ([_p, _i32, _p, _p, _p, _p], _i32),
+    "ds_cp_in_seq_local_count": ([_p, _i32, _i32, _i32], _i32),
+    "cp_split_metadata_in_seq": ([_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
+                                  _p, _i64, _p], _i32),
     "kv_rerange": ([_p, _i32, _i32, _i32, _i64, _p, _p], _i32),
     "kv_cache_write": ([_p, _i32, _i64, _p, _p, _i32, _p, _i32, _i32, _p, _i64, _p], _i32),
     "indexer_topk_workspace_size": ([_i32, _i32], _sz),
@@ -154,6 +158,50 @@ def cp_split_metadata(cu_seqlens: torch.Tensor, num_tokens: int, cp_size: int,
         _ptr(res["kv_len"]), _ptr(rows_src), _ptr(res.get("rows")), row_bytes,
         _stream(stream))
     _check("cp_split_metadata", st)
+    return res
+
+
+def cp_in_seq_local_count(cu_seqlens_host, cp_size: int, cp_rank: int) -> int:
+    """Tokens of rank cp_rank under the in-sequence split (host offsets)."""
+    cu = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+    n = lib.ds_cp_in_seq_local_count(ctypes.cast(cu, ctypes.c_void_p), len(cu_seqlens_host) - 1,
+                                     cp_size, cp_rank)
+    if n < 0:
+        raise ValueError("invalid cu_seqlens / cp_size / cp_rank")
+    return n
+
+
+def cp_split_metadata_in_seq(cu_seqlens: torch.Tensor, num_tokens: int, cp_size: int,
+                             cp_rank: int, n_local: int | None = None,
+                             rows_src: torch.Tensor | None = None, out: dict | None = None,
+                             stream=None) -> dict:
+    """Contrast mode (in-sequence split).  Same fields as cp_split_metadata;
+    n_local defaults to the count from a host copy of cu_seqlens."""
+    dev = cu_seqlens.device
+    B = cu_seqlens.numel() - 1
+    if n_local is None:
+        n_local = cp_in_seq_local_count(cu_seqlens.cpu().tolist(), cp_size, cp_rank)
+    out = dict(out or {})
+    res = {
+        "local_cu": _i32buf(B + 1, dev, out.get("local_cu")),
+        "batch_idx": _i32buf(n_local, dev, out.get("batch_idx")),
+        "global_idx": _i32buf(n_local, dev, out.get("global_idx")),
+        "kv_start": _i32buf(n_local, dev, out.get("kv_start")),
+        "kv_len": _i32buf(n_local, dev, out.get("kv_len")),
+    }
+    row_bytes = 0
+    if rows_src is not None:
+        row_bytes = rows_src.element_size() * math.prod(rows_src.shape[1:])
+        rows = out.get("rows")
+        if rows is None:
+            rows = torch.empty((n_local,) + tuple(rows_src.shape[1:]), dtype=rows_src.dtype,
+                               device=dev)
+        res["rows"] = rows
+    st = lib.cp_split_metadata_in_seq(
+        _ptr(cu_seqlens), B, num_tokens, cp_size, cp_rank, n_local, _ptr(res["local_cu"]),
+        _ptr(res["batch_idx"]), _ptr(res["global_idx"]), _ptr(res["kv_start"]),
+        _ptr(res["kv_len"]), _ptr(rows_src), _ptr(res.get("rows")), row_bytes, _stream(stream))
+    _check("cp_split_metadata_in_seq", st)
     return res
 
 
@@ -334,11 +382,16 @@ def sparse_mla_decode_noalloc(q, kv, topk_idx, sm_scale: float, d_latent: int, *
     return out, lse
 
 
-def decode_metadata(lengths: torch.Tensor) -> dict:
-    """Decode step metadata: request i has one query whose causal keys are
-    positions 0 .. L_i - 1 of that request (its own KV already cached)."""
+def decode_metadata(lengths: torch.Tensor, out: dict | None = None, stream=None) -> dict:
+    """Decode step metadata (q_req, kv_start, kv_len) from the per-request
+    context lengths (int32 on the device)."""
+    if lengths.dtype != torch.int32:
+        raise TypeError("lengths must be int32")
     n = lengths.numel()
     dev = lengths.device
-    return {"q_req": torch.arange(n, dtype=torch.int32, device=dev),
-            "kv_start": torch.zeros(n, dtype=torch.int32, device=dev),
-            "kv_len": lengths.to(torch.int32).contiguous()}
+    out = dict(out or {})
+    res = {k: _i32buf(n, dev, out.get(k)) for k in ("q_req", "kv_start", "kv_len")}
+    st = lib.decode_metadata(_ptr(lengths), n, _ptr(res["q_req"]), _ptr(res["kv_start"]),
+                             _ptr(res["kv_len"]), _stream(stream))
+    _check("decode_metadata", st)
+    return res

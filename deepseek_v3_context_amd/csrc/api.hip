@@ -81,7 +81,7 @@ using namespace ds32cp;
 
 extern "C" {
 
-int32_t ds_abi_version(void) { return 2; }
+int32_t ds_abi_version(void) { return 3; }
 
 const char* ds_last_error(void) { return g_last_error.c_str(); }
 
@@ -114,6 +114,52 @@ ds_status cp_split_metadata(const int32_t* cu_seqlens, int32_t num_reqs,
                                        kv_len, stream);
   if (st != DS_OK || rows_src == nullptr) return st;
   return launch_row_gather_rr(rows_src, rows_dst, n, cp_size, cp_rank, row_bytes, stream);
+}
+
+int32_t ds_cp_in_seq_local_count(const int32_t* cu_seqlens, int32_t num_reqs, int32_t cp_size,
+                                 int32_t cp_rank) {
+  if (cp_size < 1 || cp_rank < 0 || cp_rank >= cp_size || num_reqs < 1 || cu_seqlens == nullptr)
+    return -1;
+  int64_t n = 0;
+  for (int32_t b = 0; b < num_reqs; ++b) {
+    const int64_t len = static_cast<int64_t>(cu_seqlens[b + 1]) - cu_seqlens[b];
+    if (len < 0) return -1;
+    const int64_t c = (len + cp_size - 1) / cp_size;
+    const int64_t left = len - cp_rank * c;
+    n += left <= 0 ? 0 : (left < c ? left : c);
+  }
+  return n > INT32_MAX ? -1 : static_cast<int32_t>(n);
+}
+
+ds_status cp_split_metadata_in_seq(const int32_t* cu_seqlens, int32_t num_reqs,
+                                   int32_t num_tokens, int32_t cp_size, int32_t cp_rank,
+                                   int32_t n_local, int32_t* local_cu, int32_t* batch_idx,
+                                   int32_t* global_idx, int32_t* kv_start, int32_t* kv_len,
+                                   const void* rows_src, void* rows_dst, int64_t row_bytes,
+                                   hipStream_t stream) {
+  const char* f = "cp_split_metadata_in_seq";
+  DS_REQUIRE(cp_size >= 1, DS_ERR_INVALID_ARG, std::string(f) + ": cp_size must be >= 1");
+  DS_REQUIRE(cp_rank >= 0 && cp_rank < cp_size, DS_ERR_INVALID_ARG,
+             std::string(f) + ": cp_rank outside [0, cp_size)");
+  DS_REQUIRE(num_tokens >= 0 && n_local >= 0, DS_ERR_INVALID_ARG,
+             std::string(f) + ": num_tokens and n_local must be >= 0");
+  DS_REQUIRE(num_reqs >= 1, DS_ERR_INVALID_ARG, std::string(f) + ": num_reqs must be >= 1");
+  DS_REQUIRE(cu_seqlens != nullptr && local_cu != nullptr, DS_ERR_INVALID_ARG,
+             std::string(f) + ": cu_seqlens and local_cu are required");
+  DS_REQUIRE(rows_src == nullptr ||
+                 (row_bytes > 0 && ((global_idx != nullptr && rows_dst != nullptr) || n_local == 0)),
+             DS_ERR_INVALID_ARG,
+             std::string(f) + ": row gather needs global_idx, rows_dst and row_bytes > 0");
+  return launch_in_seq_split(cu_seqlens, num_reqs, num_tokens, cp_size, cp_rank, n_local,
+                             local_cu, batch_idx, global_idx, kv_start, kv_len, rows_src,
+                             rows_dst, row_bytes, stream);
+}
+
+ds_status decode_metadata(const int32_t* lengths, int32_t n_req, int32_t* q_req,
+                          int32_t* kv_start, int32_t* kv_len, hipStream_t stream) {
+  DS_REQUIRE(n_req >= 0, DS_ERR_INVALID_ARG, "decode_metadata: n_req < 0");
+  DS_REQUIRE(n_req == 0 || lengths != nullptr, DS_ERR_INVALID_ARG, "decode_metadata: NULL lengths");
+  return launch_decode_metadata(lengths, n_req, q_req, kv_start, kv_len, stream);
 }
 
 ds_status kv_rerange(const void* src, int32_t slot_rows, int32_t num_tokens,

@@ -97,6 +97,13 @@ ds_status launch_split_metadata(const int32_t* cu, int32_t B, int32_t T, int32_t
                                 int32_t* batch_idx, int32_t* global_idx,
                                 int32_t* kv_start, int32_t* kv_len,
                                 hipStream_t s);
+ds_status launch_in_seq_split(const int32_t* cu, int32_t B, int32_t T, int32_t cp, int32_t r,
+                              int32_t n, int32_t* local_cu, int32_t* batch_idx,
+                              int32_t* global_idx, int32_t* kv_start, int32_t* kv_len,
+                              const void* rows_src, void* rows_dst, int64_t row_bytes,
+                              hipStream_t s);
+ds_status launch_decode_metadata(const int32_t* lengths, int32_t n, int32_t* q_req,
+                                 int32_t* kv_start, int32_t* kv_len, hipStream_t s);
 ds_status launch_row_gather_rr(const void* src, void* dst, int32_t n, int32_t cp,
                                int32_t r, int64_t row_bytes, hipStream_t s);
 ds_status launch_rerange(const void* src, void* dst, int32_t T, int32_t cp,

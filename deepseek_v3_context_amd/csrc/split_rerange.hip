@@ -1,4 +1,5 @@
-// Step 1 (round-robin split + metadata) and step 2 (KV rerange).
+// Step 1 (round-robin split + metadata; the in-sequence split it replaces,
+// for contrast) and step 2 (KV rerange).
 //
 // Sources: "[DeepSeek v3.2] 上下文并行详解", section 1 and section 2B
 // (token g goes to rank g mod cp_size; the rank's sequence lengths, batch
@@ -46,10 +47,96 @@ split_metadata_kernel(const int32_t* __restrict__ cu, int32_t B, int32_t T,
   }
 }
 
-// dst row j <- src row src_row(j), vectors of type V.
+// ------------------------------------------------------------------
+// In-sequence split (the contrast mode of the same page, section 4 part 1):
+// request b of L_b tokens is cut into chunks of c_b = ceil(L_b / cp) tokens
+// and rank r takes chunk r, positions [r c_b, min(L_b, (r+1) c_b)).
+__device__ __forceinline__ int32_t in_seq_chunk(int32_t len, int32_t cp) {
+  return static_cast<int32_t>((static_cast<int64_t>(len) + cp - 1) / cp);
+}
+__device__ __forceinline__ int32_t in_seq_count(int32_t len, int32_t cp, int32_t r) {
+  const int64_t c = in_seq_chunk(len, cp);
+  const int64_t left = static_cast<int64_t>(len) - r * c;
+  return static_cast<int32_t>(left <= 0 ? 0 : (left < c ? left : c));
+}
+
+// local_cu[b] = the rank's tokens in requests before b: one workgroup scans
+// the per-request counts 1024 at a time (wave scans with row shuffles, then
+// across the 16 waves), carrying the running total between rounds.
+__global__ void __launch_bounds__(1024)
+in_seq_local_cu_kernel(const int32_t* __restrict__ cu, int32_t B, int32_t cp, int32_t r,
+                       int32_t* __restrict__ local_cu) {
+  __shared__ int32_t wave_sum[1024 / kWave];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    carry = 0;
+    local_cu[0] = 0;
+  }
+  __syncthreads();
+  for (int32_t base = 0; base < B; base += 1024) {
+    const int32_t b = base + tid;
+    int32_t v = b < B ? in_seq_count(cu[b + 1] - cu[b], cp, r) : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t u = __shfl_up(v, off);
+      if (lane >= off) v += u;
+    }
+    if (lane == kWave - 1) wave_sum[wave] = v;
+    __syncthreads();
+    int32_t before = carry;
+    for (int w = 0; w < wave; ++w) before += wave_sum[w];
+    if (b < B) local_cu[b + 1] = before + v;
+    __syncthreads();
+    if (tid == 1023) carry = before + v;
+    __syncthreads();
+  }
+}
+
+// One thread per local token j: its request b (the last b with
+// local_cu[b] <= j, so empty requests are skipped), position
+// p = r c_b + (j - local_cu[b]), global index cu[b] + p.  Entries past the
+// rank's token count (when the caller's n exceeds it) get batch and global
+// index -1 and an empty causal range.
+__global__ void __launch_bounds__(256)
+in_seq_token_kernel(const int32_t* __restrict__ cu, int32_t B, int32_t cp, int32_t r, int32_t n,
+                    const int32_t* __restrict__ local_cu, int32_t* __restrict__ batch_idx,
+                    int32_t* __restrict__ global_idx, int32_t* __restrict__ kv_start,
+                    int32_t* __restrict__ kv_len) {
+  const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  if (j >= local_cu[B]) {
+    if (batch_idx) batch_idx[j] = -1;
+    if (global_idx) global_idx[j] = -1;
+    if (kv_start) kv_start[j] = 0;
+    if (kv_len) kv_len[j] = 0;
+    return;
+  }
+  int32_t lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (local_cu[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  const int32_t p = r * in_seq_chunk(cu[lo + 1] - cu[lo], cp) + (j - local_cu[lo]);
+  if (batch_idx) batch_idx[j] = lo;
+  if (global_idx) global_idx[j] = cu[lo] + p;
+  if (kv_start) kv_start[j] = cu[lo];
+  if (kv_len) kv_len[j] = p + 1;
+}
+
+// dst row j <- src row src_row(j), vectors of type V (rows mapped to a
+// negative index are skipped).
 struct GatherRR {  // split: dst j <- src r + j*cp
   int32_t cp, r;
   __device__ int64_t operator()(int64_t j) const { return r + j * cp; }
+};
+struct GatherIdx {   // in-sequence split: dst j <- src idx[j] (skipped outside [0, limit))
+  const int32_t* idx;
+  int32_t limit;
+  __device__ int64_t operator()(int64_t j) const {
+    const int32_t g = idx[j];
+    return (g >= 0 && g < limit) ? g : -1;
+  }
 };
 struct Rerange {   // rerange: dst g <- src (g mod cp)*slot + g div cp
   int32_t cp, slot;
@@ -68,7 +155,8 @@ row_permute_kernel(const V* __restrict__ src, V* __restrict__ dst,
        e < total; e += stride) {
     const int64_t row = e / vecs_per_row;
     const int64_t col = e - row * vecs_per_row;
-    dst[e] = src[map(row) * vecs_per_row + col];
+    const int64_t from = map(row);
+    if (from >= 0) dst[e] = src[from * vecs_per_row + col];
   }
 }
 
@@ -190,6 +278,44 @@ ds_status launch_row_gather_rr(const void* src, void* dst, int32_t n, int32_t cp
                                int32_t r, int64_t row_bytes, hipStream_t s) {
   return launch_permute(src, dst, n, row_bytes, GatherRR{cp, r}, s,
                         "cp_split_metadata row gather");
+}
+
+ds_status launch_in_seq_split(const int32_t* cu, int32_t B, int32_t T, int32_t cp, int32_t r,
+                              int32_t n, int32_t* local_cu, int32_t* batch_idx,
+                              int32_t* global_idx, int32_t* kv_start, int32_t* kv_len,
+                              const void* rows_src, void* rows_dst, int64_t row_bytes,
+                              hipStream_t s) {
+  in_seq_local_cu_kernel<<<1, 1024, 0, s>>>(cu, B, cp, r, local_cu);
+  ds_status st = check_launch("cp_split_metadata_in_seq (offsets)");
+  if (st != DS_OK || n == 0) return st;
+  in_seq_token_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, s>>>(
+      cu, B, cp, r, n, local_cu, batch_idx, global_idx, kv_start, kv_len);
+  st = check_launch("cp_split_metadata_in_seq");
+  if (st != DS_OK || rows_src == nullptr) return st;
+  return launch_permute(rows_src, rows_dst, n, row_bytes, GatherIdx{global_idx, T}, s,
+                        "cp_split_metadata_in_seq row gather");
+}
+
+// Decode step metadata: request i has one query at position L_i - 1 whose
+// causal keys are positions 0 .. L_i - 1 of the request (its own KV is
+// already cached); negative lengths give an empty range.
+__global__ void __launch_bounds__(256)
+decode_metadata_kernel(const int32_t* __restrict__ lengths, int32_t n, int32_t* __restrict__ q_req,
+                       int32_t* __restrict__ kv_start, int32_t* __restrict__ kv_len) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t L = lengths[i];
+  if (q_req) q_req[i] = i;
+  if (kv_start) kv_start[i] = 0;
+  if (kv_len) kv_len[i] = L > 0 ? L : 0;
+}
+
+ds_status launch_decode_metadata(const int32_t* lengths, int32_t n, int32_t* q_req,
+                                 int32_t* kv_start, int32_t* kv_len, hipStream_t s) {
+  if (n == 0) return DS_OK;
+  decode_metadata_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, s>>>(
+      lengths, n, q_req, kv_start, kv_len);
+  return check_launch("decode_metadata");
 }
 
 ds_status launch_rerange(const void* src, void* dst, int32_t T, int32_t cp,

@@ -71,7 +71,7 @@ typedef enum ds_status {
   DS_ERR_HIP = 4
 } ds_status;
 
-/* Version of this interface (bumped on any signature change): 2. */
+/* Version of this interface (bumped on any change to it): 3. */
 int32_t ds_abi_version(void);
 
 /* Message describing the last error returned on the calling thread. */
@@ -114,6 +114,56 @@ ds_status cp_split_metadata(const int32_t* cu_seqlens, int32_t num_reqs,
                             int32_t* kv_start, int32_t* kv_len,
                             const void* rows_src, void* rows_dst,
                             int64_t row_bytes, hipStream_t stream);
+
+/* Decode step metadata, the decode counterpart of cp_split_metadata: one
+ * query per request; request i's query sits at position lengths[i] - 1 and
+ * its own KV is already in the cache ([BLOG] section 4 part 3, step D:
+ * each rank keeps its tokens' KV for the decode steps), so its causal keys
+ * are positions 0 .. lengths[i] - 1 of that request.
+ *   lengths [n_req] dev int32   context length of each request (< 0 read as 0)
+ *   q_req, kv_start, kv_len [n_req] dev int32 outputs (any may be NULL):
+ *   q_req[i] = i, kv_start[i] = 0, kv_len[i] = lengths[i]
+ * Errors: INVALID_ARG for n_req < 0 or NULL lengths with n_req > 0. */
+ds_status decode_metadata(const int32_t* lengths, int32_t n_req, int32_t* q_req,
+                          int32_t* kv_start, int32_t* kv_len, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Contrast mode: the in-sequence split that the round-robin split replaces.
+ * [BLOG] section 4 part 1: each request is cut into cp_size consecutive
+ * chunks and rank r takes chunk r of every request (8000 tokens on 8
+ * ranks: rank 0 tokens 0..999, rank 1 1000..1999, ...; with a second,
+ * 800-token request rank 0 also takes its tokens 0..99).  Reading taken:
+ * chunks of ceil(L / cp_size) tokens at token granularity (the last chunks
+ * of a request may be shorter or empty).  Not on the hot path: it exists to
+ * measure the per-rank imbalance the page describes.
+ *
+ * ds_cp_in_seq_local_count: host only, pure; cu_seqlens is a HOST array
+ * [num_reqs+1].  Returns the rank's token count, or -1 for invalid
+ * arguments (cp_size < 1, cp_rank outside [0, cp_size), num_reqs < 1,
+ * NULL, decreasing offsets).
+ *
+ * cp_split_metadata_in_seq: the same outputs as cp_split_metadata, for the
+ * rank's n_local tokens in request order and position order within a
+ * request (n_local from ds_cp_in_seq_local_count; entries past the rank's
+ * real count get batch_idx = global_idx = -1, kv_start = kv_len = 0).
+ * local_cu is required (the per-token pass reads it).  The optional row
+ * gather rows_dst[j] = rows_src[global_idx[j]] needs global_idx and skips
+ * entries outside [0, num_tokens).
+ * Errors: INVALID_ARG for cp_size < 1, cp_rank outside [0, cp_size),
+ * num_tokens or n_local < 0, num_reqs < 1, NULL cu_seqlens or local_cu, a
+ * row gather without global_idx, rows_dst (n_local > 0) or row_bytes > 0.
+ * ------------------------------------------------------------------- */
+int32_t ds_cp_in_seq_local_count(const int32_t* cu_seqlens, int32_t num_reqs,
+                                 int32_t cp_size, int32_t cp_rank);
+
+ds_status cp_split_metadata_in_seq(const int32_t* cu_seqlens, int32_t num_reqs,
+                                   int32_t num_tokens, int32_t cp_size,
+                                   int32_t cp_rank, int32_t n_local,
+                                   int32_t* local_cu, int32_t* batch_idx,
+                                   int32_t* global_idx, int32_t* kv_start,
+                                   int32_t* kv_len, const void* rows_src,
+                                   void* rows_dst, int64_t row_bytes,
+                                   hipStream_t stream);
 
 /* ---------------------------------------------------------------------
  * Step 2: rerange of the all-gathered KV into logical token order.

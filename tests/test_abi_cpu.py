@@ -9,6 +9,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 import torch
 
@@ -41,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_local_count():
-    assert ds.abi_version() == 2
+    assert ds.abi_version() == 3
     for T in (0, 1, 7, 8, 9, 8000, 25305, 65536):
         for cp in (1, 3, 8):
             for r in range(cp):
@@ -145,3 +147,54 @@ def test_mla_rejects_unsupported_dims_and_workspace():
 def test_workspace_sizes():
     assert ds.indexer_topk_workspace_size(1000, 8000) >= 1000 * 8000 * 4
     assert ds.sparse_mla_workspace_size(32, 128, 512, 2048) >= 32 * 128 * 512 * 4
+
+
+def test_in_seq_local_count_matches_the_oracle():
+    rng = np.random.default_rng(7)
+    cases = [[0, 8000], [0, 8000, 8800, 8805], [0, 8000, 8800, 8805, 11805, 13305, 25305],
+             [0, 0, 3, 3, 17], [0, 1]]
+    for _ in range(20):
+        lens = rng.integers(0, 50, size=int(rng.integers(1, 6)))
+        cases.append([0] + np.cumsum(lens).tolist())
+    for cu in cases:
+        for cp in (1, 2, 3, 8):
+            for r in range(cp):
+                want = rr.in_seq_split_metadata(cu, cp, r)["global_idx"].size
+                assert ds.cp_in_seq_local_count(cu, cp, r) == want, (cu, cp, r)
+    with pytest.raises(ValueError):
+        ds.cp_in_seq_local_count([0, 5, 3], 2, 0)        # decreasing offsets
+    with pytest.raises(ValueError):
+        ds.cp_in_seq_local_count([0, 5], 2, 2)           # rank outside [0, cp)
+
+
+def test_in_seq_split_and_decode_metadata_reject_bad_arguments_before_launch():
+    f = lib.cp_split_metadata_in_seq
+    ok = dict(cu=_p(), B=1, T=8, cp=4, r=0, n=2, lcu=_p(512), rows_src=None, gidx=_p(1024),
+              rows_dst=None, rb=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["cu"], a["B"], a["T"], a["cp"], a["r"], a["n"], a["lcu"], None, a["gidx"],
+                 None, None, a["rows_src"], a["rows_dst"], a["rb"], None)
+
+    assert call(cp=0) == 1
+    assert call(r=4) == 1 and "cp_rank" in _err()
+    assert call(n=-1) == 1
+    assert call(B=0) == 1
+    assert call(cu=None) == 1
+    assert call(lcu=None) == 1 and "local_cu" in _err()
+    assert call(rows_src=_p(4096), rows_dst=_p(8192), rb=4, gidx=None) == 1   # gather needs ids
+    assert call(rows_src=_p(4096), rows_dst=None, rb=4) == 1
+    assert lib.decode_metadata(None, -1, None, None, None, None) == 1
+    assert lib.decode_metadata(None, 3, None, None, None, None) == 1
+    assert lib.decode_metadata(None, 0, None, None, None, None) == 0
+
+
+def test_noalloc_decode_checks_like_the_workspace_variant():
+    base = lambda q_dt, kv_dt, H, dl, dr: (  # noqa: E731
+        _p(), q_dt, _p(), kv_dt, None, 100, _p(), 4, H, dl, dr, 64, 0.1, _p(), 1, None, None)
+    f = lib.sparse_mla_decode_noalloc
+    assert f(*base(1, 1, 96, 512, 64)) == 2          # head count
+    assert f(*base(1, 1, 128, 256, 64)) == 2         # latent dims
+    assert f(*base(1, 2, 128, 512, 64)) == 1         # fp8 without scale
+    assert lib.sparse_mla_decode_noalloc_scratch_bytes() == 32 << 20

@@ -43,3 +43,34 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline():
         assert w["avg_us"] > 0 and w["bytes"] > 0 and 0 < w["frac"] <= 1
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+@pytest.mark.gpu
+def test_bench_all_ranks_reports_both_split_modes():
+    env = dict(os.environ)
+    env.pop("WORLD_SIZE", None)
+    print("[bench balance] prefill_t8000_cp8, every rank, both split modes", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload",
+                        "prefill_t8000_cp8", "--all-ranks", "--steps", "2", "--warmup", "1",
+                        "--settle-ms", "0", "--cpu-seconds", "0"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=400)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
+    bal = d["rank_balance"]
+    assert set(bal) == {"round-robin", "in-seq"}
+    for mode, b in bal.items():
+        assert b["split"] == mode
+        assert len(b["ms_per_step"]) == 8 and all(t > 0 for t in b["ms_per_step"])
+        assert b["queries"] == [1000] * 8
+        mean = sum(b["ms_per_step"]) / 8
+        assert b["spread"] == pytest.approx((max(b["ms_per_step"]) - min(b["ms_per_step"])) / mean,
+                                            abs=2e-4)
+    # causal pairs per rank, in closed form: round-robin rank r has
+    # sum_j (r + 8j + 1); the in-sequence split's rank r sum_{p=1000r}^{1000r+999} (p + 1)
+    rr_pairs = [sum(r + 8 * j + 1 for j in range(1000)) for r in range(8)]
+    is_pairs = [(1000 * r + 1000) * (1000 * r + 1001) // 2 - (1000 * r) * (1000 * r + 1) // 2
+                for r in range(8)]
+    assert bal["round-robin"]["indexer_pairs"] == rr_pairs
+    assert bal["in-seq"]["indexer_pairs"] == is_pairs
+    # the contiguous split leaves rank 7 with 15x rank 0's indexer work
+    assert bal["in-seq"]["spread"] > bal["round-robin"]["spread"]
