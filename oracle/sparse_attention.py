@@ -81,9 +81,10 @@ def decode_rows(data: np.ndarray, fmt: str, scale: np.ndarray | None,
                 rows: np.ndarray) -> np.ndarray:
     """Decode the stored rows ``rows`` of a [rows, ...] tensor to float64.
 
-    ``fmt`` is ``"f32"`` (float32 values), ``"bf16"`` (uint16 bit patterns)
-    or ``"fp8"`` (uint8 e4m3fn codes; row ``r`` is multiplied by
-    ``scale[r // 128]``).
+    ``fmt`` is ``"f32"`` (float32 values), ``"bf16"`` (uint16 bit patterns),
+    ``"fp8"`` (uint8 e4m3fn codes; row ``r`` is multiplied by
+    ``scale[r // 128]``) or ``"fp8_row"`` (e4m3fn codes; row ``r`` is
+    multiplied by its own ``scale[r]``, the format the cache write encodes).
     """
     rows = np.asarray(rows, dtype=np.int64)
     picked = np.asarray(data)[rows]
@@ -97,6 +98,12 @@ def decode_rows(data: np.ndarray, fmt: str, scale: np.ndarray | None,
         vals = e4m3fn_to_f64(picked)
         s = np.asarray(scale, dtype=np.float32).astype(np.float64)
         s = s[rows // FP8_BLOCK_ROWS]
+        return vals * s.reshape((-1,) + (1,) * (vals.ndim - 1))
+    if fmt == "fp8_row":
+        if scale is None:
+            raise ValueError("fp8 rows need their per-row scale")
+        vals = e4m3fn_to_f64(picked)
+        s = np.asarray(scale, dtype=np.float32).astype(np.float64)[rows]
         return vals * s.reshape((-1,) + (1,) * (vals.ndim - 1))
     raise ValueError(f"unknown storage format {fmt!r}")
 
