@@ -357,7 +357,8 @@ def own_kv_cache_write(wl, torch, ds, st, dev, steps):
     being a few microseconds).  The host takes longer to issue a call than
     the device to run it, so a bounded spin kernel holds the stream until
     every call is queued: the pair then times the device running them back
-    to back.  Bytes per call: each own row read once and written once."""
+    to back.  Bytes per call: each own row read once and written once (the
+    fp8 write: bf16 rows read, e4m3fn codes and a scale per row written)."""
     from synth import draw_page_table
 
     print("[bench] own-KV cache write", file=sys.stderr, flush=True)
@@ -371,21 +372,41 @@ def own_kv_cache_write(wl, torch, ds, st, dev, steps):
             "kv_cache_write(indexer_k)": st["ki_cat"][r * slot: r * slot + n]}
     pools = {k: torch.empty((pool_rows,) + tuple(v.shape[1:]), dtype=v.dtype, device=dev)
              for k, v in srcs.items()}
-    per_call = {}
-    for k, v in srcs.items():
+    # fp8 on write: the rank's own rows in bf16 (as its projections produce
+    # them; seeded N(0,1)/sqrt(D) values of the rows' shape) encoded into
+    # pools with a scale per row
+    g = torch.Generator(device=dev).manual_seed(wl.seed)
+    fp8_srcs = {"kv_cache_write_fp8(latent)": wl.d_qk, "kv_cache_write_fp8(indexer_k)": wl.d_idx}
+    fp8_rows = {k: (torch.randn((n, d), generator=g, device=dev) * d ** -0.5).bfloat16()
+                for k, d in fp8_srcs.items()}
+    fp8_pools = {k: (torch.empty((pool_rows, d), dtype=torch.uint8, device=dev),
+                     torch.empty(pool_rows, dtype=torch.float32, device=dev))
+                 for k, d in fp8_srcs.items()}
+
+    def timed(call):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda._sleep(60000 * steps)   # ~25 us of device time per queued call
         ev0.record()
         for _ in range(steps):
-            ds.kv_cache_write(v, m["batch_idx"], m["local_cu"], table_d, 64, pools[k])
+            call()
         ev1.record()
         torch.cuda.synchronize()
-        per_call[k] = ev0.elapsed_time(ev1) / steps
+        return ev0.elapsed_time(ev1) / steps
+
+    per_call, nbytes = {}, {}
+    for k, v in srcs.items():
+        per_call[k] = timed(lambda: ds.kv_cache_write(v, m["batch_idx"], m["local_cu"], table_d,
+                                                      64, pools[k]))
+        nbytes[k] = 2 * n * v.element_size() * v[0].numel() if n else 0
+    for k, d in fp8_srcs.items():
+        codes, scales = fp8_pools[k]
+        per_call[k] = timed(lambda: ds.kv_cache_write_fp8(fp8_rows[k], m["batch_idx"], m["local_cu"],
+                                                          table_d, 64, codes, scales))
+        nbytes[k] = n * (2 * d + d + 4)       # bf16 rows read, codes and scales written
     out = {}
     for k, ms in per_call.items():
-        nbytes = 2 * n * srcs[k].element_size() * srcs[k][0].numel() if n else 0
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out[k] = {"avg_us": round(ms * 1e3, 2), "bytes": nbytes, "gbs": round(gbs, 1),
+        gbs = nbytes[k] / (ms * 1e-3) / 1e9
+        out[k] = {"avg_us": round(ms * 1e3, 2), "bytes": nbytes[k], "gbs": round(gbs, 1),
                   "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     return out
 

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("DS32CP_LIB", os.path.join(_HERE, "libds32cp.so"))
 
-DS_F32, DS_BF16, DS_FP8_E4M3FN = 0, 1, 2
+DS_F32, DS_BF16, DS_FP8_E4M3FN, DS_FP8_E4M3FN_ROWSCALE = 0, 1, 2, 3
 STATUS = {0: "DS_OK", 1: "DS_ERR_INVALID_ARG", 2: "DS_ERR_UNSUPPORTED",
           3: "DS_ERR_WORKSPACE", 4: "DS_ERR_HIP"}
 
@@ -54,6 +54,8 @@ _SIGS = {
                                   _p, _i64, _p], _i32),
     "kv_rerange": ([_p, _i32, _i32, _i32, _i64, _p, _p], _i32),
     "kv_cache_write": ([_p, _i32, _i64, _p, _p, _i32, _p, _i32, _i32, _p, _i64, _p], _i32),
+    "kv_cache_write_fp8": ([_p, _i32, _i32, _i32, _p, _p, _i32, _p, _i32, _i32, _p, _p, _i64,
+                            _p], _i32),
     "indexer_topk_workspace_size": ([_i32, _i32], _sz),
     "indexer_topk": ([_p, _i32, _p, _p, _i32, _p, _i64, _p, _p, _p, _p, _i32, _i32,
                       _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _sz, _p], _i32),
@@ -100,13 +102,15 @@ def _stream(stream):
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2}
 
 
-def dtype_code(t: torch.Tensor) -> int:
+def dtype_code(t: torch.Tensor, scale_per_row: bool = False) -> int:
+    """Storage code of a tensor; fp8 tensors carry one scale per 128 rows,
+    or one per row with scale_per_row (the pools kv_cache_write_fp8 fills)."""
     if t.dtype == torch.float32:
         return DS_F32
     if t.dtype == torch.bfloat16:
         return DS_BF16
     if t.dtype == torch.float8_e4m3fn:
-        return DS_FP8_E4M3FN
+        return DS_FP8_E4M3FN_ROWSCALE if scale_per_row else DS_FP8_E4M3FN
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -241,6 +245,31 @@ def kv_cache_write(rows: torch.Tensor, batch_idx: torch.Tensor, local_cu: torch.
     return pool
 
 
+def kv_cache_write_fp8(rows: torch.Tensor, batch_idx: torch.Tensor, local_cu: torch.Tensor,
+                       page_table: torch.Tensor, page_size: int, pool_codes: torch.Tensor,
+                       pool_scale: torch.Tensor, stream=None):
+    """Step D with fp8 encoding: the rank's own bf16 rows [n_local, D] are
+    encoded per row into the pool (codes [pool_rows, D] float8_e4m3fn or
+    uint8, scales [pool_rows] fp32), in place; returns (pool_codes,
+    pool_scale).  The pool then reads back with scale_per_row=True."""
+    if rows.dtype != torch.bfloat16 or rows.dim() != 2:
+        raise ValueError("rows must be a 2-d bf16 tensor")
+    if tuple(pool_codes.shape[1:]) != tuple(rows.shape[1:]) or pool_codes.element_size() != 1:
+        raise ValueError("pool_codes must be [pool_rows, D] of one-byte codes")
+    if pool_scale.dtype != torch.float32 or pool_scale.numel() < pool_codes.shape[0]:
+        raise ValueError("pool_scale must be fp32 with a scale per pool row")
+    for name, t in (("batch_idx", batch_idx), ("local_cu", local_cu), ("page_table", page_table)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    n_req = local_cu.numel() - 1
+    st = lib.kv_cache_write_fp8(_ptr(rows), DS_BF16, rows.shape[0], rows.shape[1], _ptr(batch_idx),
+                                _ptr(local_cu), n_req, _ptr(page_table), page_table.shape[1],
+                                page_size, _ptr(pool_codes), _ptr(pool_scale),
+                                pool_codes.shape[0], _stream(stream))
+    _check("kv_cache_write_fp8", st)
+    return pool_codes, pool_scale
+
+
 def indexer_topk_workspace_size(n_q: int, max_kv_len: int) -> int:
     return lib.indexer_topk_workspace_size(n_q, max_kv_len)
 
@@ -255,7 +284,7 @@ def _paging(q_req, page_table, page_size):
 def indexer_topk(q_idx, w, k_idx, kv_start, kv_len, max_kv_len: int, topk: int,
                  k_scale=None, q_req=None, page_table=None, page_size: int = 0,
                  topk_idx=None, topk_score=None, want_score: bool = False,
-                 workspace=None, stream=None):
+                 workspace=None, scale_per_row: bool = False, stream=None):
     """Steps 3 + 4.  Returns (topk_idx [n_q, topk] int32, topk_score or None)."""
     n_q, h_idx, d_idx = q_idx.shape
     dev = q_idx.device
@@ -268,7 +297,7 @@ def indexer_topk(q_idx, w, k_idx, kv_start, kv_len, max_kv_len: int, topk: int,
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     qr, pt, n_req, ps, mp = _paging(q_req, page_table, page_size)
     st = lib.indexer_topk(
-        _ptr(q_idx), dtype_code(q_idx), _ptr(w), _ptr(k_idx), dtype_code(k_idx),
+        _ptr(q_idx), dtype_code(q_idx), _ptr(w), _ptr(k_idx), dtype_code(k_idx, scale_per_row),
         _ptr(k_scale), k_idx.shape[0], _ptr(kv_start), _ptr(kv_len), qr, pt, n_req, ps, mp,
         n_q, h_idx, d_idx, max_kv_len, topk, _ptr(topk_idx), _ptr(topk_score),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
@@ -278,7 +307,7 @@ def indexer_topk(q_idx, w, k_idx, kv_start, kv_len, max_kv_len: int, topk: int,
 
 def indexer_scores(q_idx, w, k_idx, kv_start, kv_len, max_kv_len: int, k_scale=None,
                    q_req=None, page_table=None, page_size: int = 0, scores=None,
-                   stream=None) -> torch.Tensor:
+                   scale_per_row: bool = False, stream=None) -> torch.Tensor:
     """Step 3 alone: scores [n_q, max_kv_len] fp32 (entries past kv_len are
     left as allocated: NaN when allocated here)."""
     n_q, h_idx, d_idx = q_idx.shape
@@ -287,7 +316,7 @@ def indexer_scores(q_idx, w, k_idx, kv_start, kv_len, max_kv_len: int, k_scale=N
                             device=q_idx.device)
     qr, pt, n_req, ps, mp = _paging(q_req, page_table, page_size)
     st = lib.indexer_scores(
-        _ptr(q_idx), dtype_code(q_idx), _ptr(w), _ptr(k_idx), dtype_code(k_idx),
+        _ptr(q_idx), dtype_code(q_idx), _ptr(w), _ptr(k_idx), dtype_code(k_idx, scale_per_row),
         _ptr(k_scale), k_idx.shape[0], _ptr(kv_start), _ptr(kv_len), qr, pt, n_req, ps, mp,
         n_q, h_idx, d_idx, max_kv_len, _ptr(scores), scores.shape[1], _stream(stream))
     _check("indexer_scores", st)
@@ -324,7 +353,7 @@ def sparse_mla_prefill_workspace_size(kv_rows: int, kv_dtype) -> int:
 
 def sparse_mla_prefill(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale=None,
                        out=None, out_dtype=None, lse=None, want_lse: bool = True,
-                       workspace=None, stream=None):
+                       workspace=None, scale_per_row: bool = False, stream=None):
     """Step 5 (prefill).  Returns (out [n_q, H, d_latent], lse [n_q, H] or None).
     fp8 kv needs a workspace (allocated here when not given)."""
     out_dtype = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
@@ -336,7 +365,7 @@ def sparse_mla_prefill(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.sparse_mla_prefill(
-        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv), _ptr(kv_scale), kv.shape[0],
+        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv, scale_per_row), _ptr(kv_scale), kv.shape[0],
         _ptr(topk_idx), n_q, H, d_latent, d_rope, topk_idx.shape[1], sm_scale, _ptr(out),
         dtype_code(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check("sparse_mla_prefill", st)
@@ -349,7 +378,7 @@ def sparse_mla_workspace_size(n_q: int, n_heads: int, d_latent: int, topk: int) 
 
 def sparse_mla_decode(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale=None,
                       out=None, out_dtype=None, lse=None, want_lse: bool = True,
-                      workspace=None, stream=None):
+                      workspace=None, scale_per_row: bool = False, stream=None):
     """Step 5 (decode: rows split across workgroups, merged by LSE)."""
     out_dtype = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
     n_q, H, d_rope, out = _mla_common(q, kv, topk_idx, d_latent, out, out_dtype)
@@ -360,7 +389,7 @@ def sparse_mla_decode(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale=
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     st = lib.sparse_mla_decode(
-        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv), _ptr(kv_scale), kv.shape[0],
+        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv, scale_per_row), _ptr(kv_scale), kv.shape[0],
         _ptr(topk_idx), n_q, H, d_latent, d_rope, topk, sm_scale, _ptr(out), dtype_code(out),
         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
@@ -369,13 +398,13 @@ def sparse_mla_decode(q, kv, topk_idx, sm_scale: float, d_latent: int, kv_scale=
 
 
 def sparse_mla_decode_noalloc(q, kv, topk_idx, sm_scale: float, d_latent: int, *, out,
-                              lse=None, kv_scale=None, stream=None):
+                              lse=None, kv_scale=None, scale_per_row: bool = False, stream=None):
     """Step 5 (decode) with the library's own scratch for the split partials:
     nothing is allocated, by this call or the library; the caller passes
     every output buffer."""
     n_q, H, d_qk = q.shape
     st = lib.sparse_mla_decode_noalloc(
-        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv), _ptr(kv_scale), kv.shape[0],
+        _ptr(q), dtype_code(q), _ptr(kv), dtype_code(kv, scale_per_row), _ptr(kv_scale), kv.shape[0],
         _ptr(topk_idx), n_q, H, d_latent, d_qk - d_latent, topk_idx.shape[1], sm_scale, _ptr(out),
         dtype_code(out), _ptr(lse), _stream(stream))
     _check("sparse_mla_decode_noalloc", st)

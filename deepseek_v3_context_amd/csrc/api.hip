@@ -209,6 +209,33 @@ ds_status kv_cache_write(const void* rows, int32_t n_local, int64_t row_bytes,
                                page_table, max_pages, page_size, pool, pool_rows, stream);
 }
 
+ds_status kv_cache_write_fp8(const void* rows, ds_dtype rows_dtype, int32_t n_local,
+                             int32_t row_elems, const int32_t* batch_idx, const int32_t* local_cu,
+                             int32_t n_req, const int32_t* page_table, int32_t max_pages,
+                             int32_t page_size, uint8_t* pool_codes, float* pool_scale,
+                             int64_t pool_rows, hipStream_t stream) {
+  const char* f = "kv_cache_write_fp8";
+  DS_REQUIRE(rows_dtype == DS_BF16, DS_ERR_UNSUPPORTED, std::string(f) + ": rows must be bf16");
+  DS_REQUIRE(n_local >= 0 && n_req >= 0 && max_pages >= 0 && pool_rows >= 0,
+             DS_ERR_INVALID_ARG, std::string(f) + ": negative size");
+  DS_REQUIRE(page_size >= 1, DS_ERR_INVALID_ARG, std::string(f) + ": page_size must be >= 1");
+  DS_REQUIRE(row_elems >= 1 && row_elems <= kCacheFp8MaxElems && row_elems % 4 == 0,
+             DS_ERR_UNSUPPORTED,
+             std::string(f) + ": row_elems must be a multiple of 4 in [4, 1024]");
+  if (n_local == 0) return DS_OK;
+  DS_REQUIRE(rows != nullptr && batch_idx != nullptr && local_cu != nullptr &&
+                 ((pool_codes != nullptr && pool_scale != nullptr) || pool_rows == 0) &&
+                 (page_table != nullptr || static_cast<int64_t>(n_req) * max_pages == 0),
+             DS_ERR_INVALID_ARG, std::string(f) + ": NULL buffer");
+  DS_REQUIRE((reinterpret_cast<uintptr_t>(rows) & 7) == 0 &&
+                 (reinterpret_cast<uintptr_t>(pool_codes) & 3) == 0,
+             DS_ERR_INVALID_ARG, std::string(f) + ": rows must be 8-byte and codes 4-byte aligned");
+  if (pool_rows == 0 || static_cast<int64_t>(n_req) * max_pages == 0) return DS_OK;   // nothing maps
+  return launch_kv_cache_write_fp8(rows, n_local, row_elems, batch_idx, local_cu, n_req,
+                                   page_table, max_pages, page_size, pool_codes, pool_scale,
+                                   pool_rows, stream);
+}
+
 static ds_status check_indexer(const char* fn, const IndexerArgs& a) {
   const std::string f(fn);
   DS_REQUIRE(a.n_q >= 0 && a.max_kv_len >= 0 && a.k_rows >= 0, DS_ERR_INVALID_ARG,
@@ -231,14 +258,31 @@ static ds_status check_indexer(const char* fn, const IndexerArgs& a) {
     DS_REQUIRE(a.h_idx <= 64 && a.d_idx <= 128, DS_ERR_UNSUPPORTED,
                f + ": f32 path supports h_idx <= 64, d_idx <= 128");
   } else {
-    DS_REQUIRE(a.k_dtype == DS_BF16 || a.k_dtype == DS_FP8_E4M3FN, DS_ERR_UNSUPPORTED,
-               f + ": bf16 queries need bf16 or fp8 keys");
+    DS_REQUIRE(a.k_dtype == DS_BF16 || a.k_dtype == DS_FP8_E4M3FN ||
+                   a.k_dtype == DS_FP8_E4M3FN_ROWSCALE,
+               DS_ERR_UNSUPPORTED, f + ": bf16 queries need bf16 or fp8 keys");
+    DS_REQUIRE(a.k_dtype != DS_FP8_E4M3FN_ROWSCALE || a.page_table != nullptr,
+               DS_ERR_UNSUPPORTED, f + ": fp8 keys with a scale per row are read from a paged pool");
     DS_REQUIRE(a.h_idx == 64 && a.d_idx == 128, DS_ERR_UNSUPPORTED,
                f + ": bf16 path supports h_idx == 64, d_idx == 128");
   }
-  if (a.k_dtype == DS_FP8_E4M3FN)
+  if (a.k_dtype == DS_FP8_E4M3FN || a.k_dtype == DS_FP8_E4M3FN_ROWSCALE)
     DS_REQUIRE(a.k_scale != nullptr, DS_ERR_INVALID_ARG, f + ": fp8 keys need k_scale");
   return DS_OK;
+}
+
+// The kernels see one fp8 format; the scale granularity goes in a shift.
+static void normalize_fp8(IndexerArgs& a) {
+  if (a.k_dtype == DS_FP8_E4M3FN_ROWSCALE) {
+    a.k_dtype = DS_FP8_E4M3FN;
+    a.k_scale_shift = 0;
+  }
+}
+static void normalize_fp8(MlaArgs& a) {
+  if (a.kv_dtype == DS_FP8_E4M3FN_ROWSCALE) {
+    a.kv_dtype = DS_FP8_E4M3FN;
+    a.scale_shift = 0;
+  }
 }
 
 size_t indexer_topk_workspace_size(int32_t n_q, int32_t max_kv_len) {
@@ -263,6 +307,7 @@ ds_status indexer_scores(const void* q_idx, ds_dtype q_dtype, const float* w,
   DS_REQUIRE(score_stride >= max_kv_len, DS_ERR_INVALID_ARG,
              "indexer_scores: score_stride < max_kv_len");
   DS_REQUIRE(n_q == 0 || scores != nullptr, DS_ERR_INVALID_ARG, "indexer_scores: NULL scores");
+  normalize_fp8(a);
   return launch_indexer_scores(a, stream);
 }
 
@@ -317,6 +362,7 @@ ds_status indexer_topk(const void* q_idx, ds_dtype q_dtype, const float* w,
   if (st != DS_OK) return st;
   DS_REQUIRE(ws != nullptr && ws_bytes >= indexer_topk_workspace_size(n_q, max_kv_len),
              DS_ERR_WORKSPACE, "indexer_topk: workspace smaller than indexer_topk_workspace_size()");
+  normalize_fp8(a);
   st = launch_indexer_scores(a, stream);
   if (st != DS_OK) return st;
   TopkArgs t{static_cast<const float*>(ws), stride, kv_start, kv_len, q_req, page_table,
@@ -352,8 +398,9 @@ static ds_status check_mla(const char* fn, const MlaArgs& a) {
     DS_REQUIRE(a.n_heads <= 128 && a.d_latent + a.d_rope <= 640, DS_ERR_UNSUPPORTED,
                f + ": f32 path supports n_heads <= 128, d_latent + d_rope <= 640");
   } else if (a.q_dtype == DS_BF16) {
-    DS_REQUIRE(a.kv_dtype == DS_BF16 || a.kv_dtype == DS_FP8_E4M3FN, DS_ERR_UNSUPPORTED,
-               f + ": bf16 queries need bf16 or fp8 kv");
+    DS_REQUIRE(a.kv_dtype == DS_BF16 || a.kv_dtype == DS_FP8_E4M3FN ||
+                   a.kv_dtype == DS_FP8_E4M3FN_ROWSCALE,
+               DS_ERR_UNSUPPORTED, f + ": bf16 queries need bf16 or fp8 kv");
     // the kernels run 32, 64 or 128 heads per query row (a 96-head row
     // would have them read and write a neighbouring row's heads)
     DS_REQUIRE((a.n_heads == 32 || a.n_heads == 64 || a.n_heads == 128) && a.d_latent == 512 &&
@@ -363,13 +410,13 @@ static ds_status check_mla(const char* fn, const MlaArgs& a) {
   } else {
     return fail(DS_ERR_UNSUPPORTED, f + ": q must be f32 or bf16");
   }
-  if (a.kv_dtype == DS_FP8_E4M3FN)
+  if (a.kv_dtype == DS_FP8_E4M3FN || a.kv_dtype == DS_FP8_E4M3FN_ROWSCALE)
     DS_REQUIRE(a.kv_scale != nullptr, DS_ERR_INVALID_ARG, f + ": fp8 kv needs kv_scale");
   return DS_OK;
 }
 
 size_t sparse_mla_prefill_workspace_size(int64_t kv_rows, ds_dtype kv_dtype) {
-  if (kv_dtype != DS_FP8_E4M3FN || kv_rows <= 0) return 0;
+  if ((kv_dtype != DS_FP8_E4M3FN && kv_dtype != DS_FP8_E4M3FN_ROWSCALE) || kv_rows <= 0) return 0;
   return static_cast<size_t>(kv_rows) * kMlaWidenedRowBytes;
 }
 
@@ -383,6 +430,7 @@ ds_status sparse_mla_prefill(const void* q, ds_dtype q_dtype, const void* kv,
             d_rope, topk, sm_scale, out, out_dtype, lse, 1, nullptr};
   ds_status st = check_mla("sparse_mla_prefill", a);
   if (st != DS_OK) return st;
+  normalize_fp8(a);
   const size_t need = sparse_mla_prefill_workspace_size(kv_rows, kv_dtype);
   if (need > 0) {
     DS_REQUIRE(ws != nullptr && ws_bytes >= need, DS_ERR_WORKSPACE,
@@ -414,6 +462,7 @@ ds_status sparse_mla_decode(const void* q, ds_dtype q_dtype, const void* kv,
             d_rope, topk, sm_scale, out, out_dtype, lse, 1, ws};
   ds_status st = check_mla("sparse_mla_decode", a);
   if (st != DS_OK) return st;
+  normalize_fp8(a);
   DS_REQUIRE(ws != nullptr && ws_bytes >= sparse_mla_workspace_size(n_q, n_heads, d_latent, topk),
              DS_ERR_WORKSPACE, "sparse_mla_decode: workspace smaller than sparse_mla_workspace_size()");
   if (q_dtype != DS_F32) a.n_splits = mla_decode_splits(n_q, topk);
@@ -432,6 +481,7 @@ ds_status sparse_mla_decode_noalloc(const void* q, ds_dtype q_dtype, const void*
             d_rope, topk, sm_scale, out, out_dtype, lse, 1, nullptr};
   ds_status st = check_mla("sparse_mla_decode_noalloc", a);
   if (st != DS_OK) return st;
+  normalize_fp8(a);
   if (q_dtype == DS_F32 || n_q == 0) return launch_sparse_mla(a, stream);   // no partials
   // the default split count when its partials fit the scratch, else the
   // largest count that does (one split writes the output directly)

@@ -31,6 +31,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxDevices = 64;   // per-device host caches
 constexpr int kFp8BlockRows = 128;
+constexpr int kCacheFp8MaxElems = 1024;   // kv_cache_write_fp8: elements per row
 
 // ------------------------------------------------------------ conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -108,6 +109,11 @@ ds_status launch_row_gather_rr(const void* src, void* dst, int32_t n, int32_t cp
                                int32_t r, int64_t row_bytes, hipStream_t s);
 ds_status launch_rerange(const void* src, void* dst, int32_t T, int32_t cp,
                          int32_t slot_rows, int64_t row_bytes, hipStream_t s);
+ds_status launch_kv_cache_write_fp8(const void* rows, int32_t n_local, int32_t row_elems,
+                                    const int32_t* batch_idx, const int32_t* local_cu,
+                                    int32_t n_req, const int32_t* page_table, int32_t max_pages,
+                                    int32_t page_size, uint8_t* pool_codes, float* pool_scale,
+                                    int64_t pool_rows, hipStream_t s);
 ds_status launch_kv_cache_write(const void* rows, int32_t n_local, int64_t row_bytes,
                                 const int32_t* batch_idx, const int32_t* local_cu,
                                 int32_t n_req, const int32_t* page_table,
@@ -130,6 +136,7 @@ struct IndexerArgs {
   int32_t n_q, h_idx, d_idx, max_kv_len;
   float* scores;
   int64_t score_stride;
+  int32_t k_scale_shift = 7;   // fp8 keys: scale of row r is k_scale[r >> k_scale_shift]
 };
 ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s);
 

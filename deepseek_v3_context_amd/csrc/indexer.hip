@@ -607,7 +607,7 @@ indexer_paged_mfma_kernel(IndexerArgs a) {
         if (row < 0) {
           v = -INFINITY;
         } else if constexpr (kFp8) {
-          v *= a.k_scale[row / kFp8BlockRows];
+          v *= a.k_scale[row >> a.k_scale_shift];
         }
         srow[p] = v;
       }

@@ -229,6 +229,83 @@ kv_cache_write_kernel(const V* __restrict__ src, V* __restrict__ pool, int64_t n
   }
 }
 
+// Own-KV retention with fp8 encoding: one wave per local row (the same
+// destination rule as kv_cache_write_kernel), four consecutive bf16 values
+// per lane and step (row_elems <= 1024: at most four steps, held in
+// registers).  scale = row amax / 448 (a correctly rounded fp32 division),
+// code = e4m3fn of clamp(x / scale, +-448) by gfx950's conversion
+// instruction (round to nearest even); an all-zero row stores scale 0 and
+// zero codes.
+__global__ void __launch_bounds__(256)
+kv_cache_write_fp8_kernel(const uint16_t* __restrict__ rows, int32_t n_local, int32_t D,
+                          const int32_t* __restrict__ batch_idx,
+                          const int32_t* __restrict__ local_cu, int32_t n_req,
+                          const int32_t* __restrict__ page_table, int32_t max_pages,
+                          int32_t page_size, uint8_t* __restrict__ codes,
+                          float* __restrict__ scales, int64_t pool_rows) {
+  constexpr float kE4m3Max = 448.f;
+  const int lane = threadIdx.x & 63;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  // every exit below is uniform over the wave (one row per wave)
+  if (j >= n_local) return;
+  const int32_t b = batch_idx[j];
+  if (b < 0 || b >= n_req) return;
+  const int64_t p = j - local_cu[b];
+  if (p < 0) return;
+  const int64_t pg = p / page_size;
+  if (pg >= max_pages) return;
+  const int32_t page = page_table[static_cast<int64_t>(b) * max_pages + pg];
+  if (page < 0) return;
+  const int64_t phys = static_cast<int64_t>(page) * page_size + (p - pg * page_size);
+  if (phys >= pool_rows) return;
+  const int G = D >> 2;   // groups of four values
+  float x[4][4];
+  float amax = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int g = lane + kWave * s;
+    uint2 v = make_uint2(0u, 0u);
+    if (g < G) v = *reinterpret_cast<const uint2*>(rows + j * D + 4 * g);
+    x[s][0] = bf16_bits_to_f32(static_cast<uint16_t>(v.x & 0xffffu));
+    x[s][1] = bf16_bits_to_f32(static_cast<uint16_t>(v.x >> 16));
+    x[s][2] = bf16_bits_to_f32(static_cast<uint16_t>(v.y & 0xffffu));
+    x[s][3] = bf16_bits_to_f32(static_cast<uint16_t>(v.y >> 16));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[s][e]));
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / kE4m3Max;
+  if (lane == 0) scales[phys] = scale;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int g = lane + kWave * s;
+    if (g >= G) continue;
+    uint32_t word = 0u;
+    if (scale > 0.f) {
+      float q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = fminf(fmaxf(x[s][e] / scale, -kE4m3Max), kE4m3Max);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+      word = static_cast<uint32_t>(w);
+    }
+    *reinterpret_cast<uint32_t*>(codes + phys * D + 4 * g) = word;
+  }
+}
+
+ds_status launch_kv_cache_write_fp8(const void* rows, int32_t n_local, int32_t row_elems,
+                                    const int32_t* batch_idx, const int32_t* local_cu,
+                                    int32_t n_req, const int32_t* page_table, int32_t max_pages,
+                                    int32_t page_size, uint8_t* pool_codes, float* pool_scale,
+                                    int64_t pool_rows, hipStream_t s) {
+  if (n_local == 0) return DS_OK;
+  kv_cache_write_fp8_kernel<<<static_cast<unsigned>(ceil_div(n_local, 4)), 256, 0, s>>>(
+      static_cast<const uint16_t*>(rows), n_local, row_elems, batch_idx, local_cu, n_req,
+      page_table, max_pages, page_size, pool_codes, pool_scale, pool_rows);
+  return check_launch("kv_cache_write_fp8");
+}
+
 ds_status launch_kv_cache_write(const void* rows, int32_t n_local, int64_t row_bytes,
                                 const int32_t* batch_idx, const int32_t* local_cu,
                                 int32_t n_req, const int32_t* page_table,

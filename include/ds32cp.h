@@ -35,7 +35,11 @@
  * - Arrays are dense and row-major with the shapes given; indices are
  *   int32.  bf16 arrays hold bfloat16 bit patterns; fp8 arrays hold OCP
  *   e4m3fn codes (bias 7, no infinities) with one fp32 scale per 128
- *   consecutive rows (value = code * scale[row / 128], scale >= 0).
+ *   consecutive rows (DS_FP8_E4M3FN: value = code * scale[row / 128]) or
+ *   one per row (DS_FP8_E4M3FN_ROWSCALE: value = code * scale[row]),
+ *   scale >= 0.  Keys and latent rows of either fp8 format are read by
+ *   sparse_mla_* and by the paged (decode) indexer; the contiguous
+ *   (prefill) indexer reads the per-128-row format only.
  * - Arguments are checked on the host before any launch:
  *   DS_ERR_INVALID_ARG / DS_ERR_UNSUPPORTED / DS_ERR_WORKSPACE return
  *   without touching the device.  DS_ERR_HIP reports a failed launch; the
@@ -60,7 +64,9 @@ extern "C" {
 typedef enum ds_dtype {
   DS_F32 = 0,
   DS_BF16 = 1,
-  DS_FP8_E4M3FN = 2
+  DS_FP8_E4M3FN = 2,          /* e4m3fn codes, one fp32 scale per 128 rows */
+  DS_FP8_E4M3FN_ROWSCALE = 3  /* e4m3fn codes, one fp32 scale per row
+                                 (the pools kv_cache_write_fp8 fills) */
 } ds_dtype;
 
 typedef enum ds_status {
@@ -371,6 +377,32 @@ ds_status kv_cache_write(const void* rows, int32_t n_local, int64_t row_bytes,
                          const int32_t* batch_idx, const int32_t* local_cu, int32_t n_req,
                          const int32_t* page_table, int32_t max_pages, int32_t page_size,
                          void* pool, int64_t pool_rows, hipStream_t stream);
+
+/* Step D with fp8 encoding: [BLOG] section 1 (the round-robin split lifts
+ * the old split's "no FP8 KV cache" limit) and section 4 part 3 step D.
+ * Each local row (bf16, row_elems values) is encoded on its own and stored
+ * where kv_cache_write stores it: pool_codes[phys] gets the e4m3fn codes
+ * and pool_scale[phys] the row's scale, so the pool is read back as
+ * DS_FP8_E4M3FN_ROWSCALE.  Encoding (the pages give none): scale = row
+ * amax / 448 (fp32, correctly rounded), code = e4m3fn nearest to
+ * x / scale, ties to even, with x / scale clamped to [-448, 448]; an
+ * all-zero row stores scale 0 and zero codes.  A scale per row keeps rows
+ * of different requests, written at different times, apart: no write
+ * re-encodes a row it does not own.  Rows must be finite.
+ *   rows        [n_local, row_elems] dev bf16 (rows_dtype DS_BF16), 8-byte aligned
+ *   batch_idx, local_cu, page_table, max_pages, page_size: as kv_cache_write
+ *   pool_codes  [pool_rows, row_elems] dev uint8, 4-byte aligned, in place
+ *   pool_scale  [pool_rows] dev fp32, in place
+ * Supported: row_elems a multiple of 4 in [4, 1024] (576 latent, 128
+ * indexer-key values).  Errors: UNSUPPORTED for other row sizes or row
+ * dtypes; INVALID_ARG as kv_cache_write, and for misaligned rows/codes. */
+ds_status kv_cache_write_fp8(const void* rows, ds_dtype rows_dtype, int32_t n_local,
+                             int32_t row_elems, const int32_t* batch_idx,
+                             const int32_t* local_cu, int32_t n_req,
+                             const int32_t* page_table, int32_t max_pages,
+                             int32_t page_size, uint8_t* pool_codes, float* pool_scale,
+                             int64_t pool_rows, hipStream_t stream);
+
 
 #ifdef __cplusplus
 }

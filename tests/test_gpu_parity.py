@@ -55,7 +55,7 @@ def _sample_rows(n, seed, local_cu=None):
 def _mla_gate(wl):
     if wl.kv_fmt == "f32":
         return 1e-4, 1e-4
-    if wl.kv_fmt == "fp8":
+    if wl.kv_fmt in ("fp8", "fp8_row"):
         return 6e-2, 3e-2
     return 2e-2, 1e-2
 
