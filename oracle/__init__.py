@@ -27,11 +27,14 @@ Modules:
   e4m3fn), indexer scores, top-k selection, sparse latent attention (fp64).
 * :mod:`oracle.pipeline` -- the steps chained for chosen query rows.
 * :mod:`oracle.kv_cache` -- the rank keeping its own tokens' KV in the
-  paged cache pool after attention (section 4 part 3, step D).
+  paged cache pool after attention (section 4 part 3, step D), as given or
+  encoded as fp8 with a scale per row.
+* :mod:`oracle.projections` -- the dense projections on either side of the
+  path (the indexer's and MLA's linear layers, the latent-form absorption).
 
 Parity status of each function is stated in its docstring; every function
 here is pinned by ``tests/test_oracle_*.py`` against values the pages print,
 closed forms, library routines on special cases, or brute force.
 """
 
-from . import round_robin_cp, sparse_attention, pipeline, kv_cache  # noqa: F401
+from . import round_robin_cp, sparse_attention, pipeline, kv_cache, projections  # noqa: F401
