@@ -411,6 +411,70 @@ def own_kv_cache_write(wl, torch, ds, st, dev, steps):
     return out
 
 
+# The dense projections around the path at DeepSeek-V3.2's dimensions
+# (hidden 7168, q compression 1536, 128 heads x (128 nope + 64 rope), latent
+# 512, value head 128; indexer 64 x 128): name -> (N, K, batch); M is the
+# rank's token count.
+PROJECTIONS = {
+    "mla_q_down": (1536, 7168, 1),
+    "mla_q_up": (128 * 192, 1536, 1),
+    "mla_q_absorb": (512, 128, 128),        # per head, into the latent part of q
+    "indexer_wq_b": (64 * 128, 1536, 1),
+    "indexer_w_k": (128, 7168, 1),
+    "mla_value_up": (128, 512, 128),        # per head, O_latent . W_UV
+    "o_proj": (7168, 128 * 128, 1),
+}
+
+
+def projections(wl, torch, ds, n, steps):
+    """Each projection GEMM on the rank's n tokens with seeded synthetic
+    weights (no trained weights), outside the step: `steps` back-to-back
+    calls between one event pair, the stream held by a spin kernel until
+    all are queued.  The per-head products run on the strided in-place views
+    the path uses (q_up's nope part -> the latent part of the 576-wide MLA
+    query; O_latent -> the value rows)."""
+    print("[bench] projections", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(wl.seed)
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(shape, generator=g, device=dev) * scale).bfloat16()
+
+    out = {}
+    for name, (N, K, batch) in PROJECTIONS.items():
+        if name == "mla_q_absorb":
+            q_up = rnd(n, 128, 192)
+            a, w = q_up[:, :, :128].transpose(0, 1), rnd(128, 512, 128, scale=128 ** -0.5)
+            q_mla = torch.empty((n, 128, 576), dtype=torch.bfloat16, device=dev)
+            c = q_mla[:, :, :512].transpose(0, 1)
+        elif name == "mla_value_up":
+            a, w = rnd(n, 128, 512).transpose(0, 1), rnd(128, 128, 512, scale=512 ** -0.5)
+            c = torch.empty((n, 128 * 128), dtype=torch.bfloat16, device=dev).view(n, 128, 128).transpose(0, 1)
+        else:
+            a, w = rnd(n, K), rnd(N, K, scale=K ** -0.5)
+            c = torch.empty((n, N), dtype=torch.bfloat16, device=dev)
+        need = ds.gemm_bf16_nt_workspace_size(n, N, K, batch)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ds.gemm_bf16_nt(a, w, out=c, workspace=ws)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(60000 * steps)
+        ev0.record()
+        for _ in range(steps):
+            ds.gemm_bf16_nt(a, w, out=c, workspace=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        flops = 2.0 * n * N * K * batch
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"M": n, "N": N, "K": K, "batch": batch, "avg_us": round(ms * 1e3, 2),
+                     "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "splits": 1 if need == 0 else need // (4 * n * N * batch)}
+        del a, w, c, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cold_steps(wl, torch, ds, st, step, steps):
     """The step with the Infinity Cache (MALL) flushed before each one: a
     512 MB scratch write between steps, outside the events; one event pair
@@ -581,6 +645,7 @@ def main():
         line["cold_cache"] = cold_steps(wl, torch, ds, st, step, args.steps)
     if wl.kind == "prefill":
         line["outside_step"] = own_kv_cache_write(wl, torch, ds, st, dev, args.steps)
+        line["projections"] = projections(wl, torch, ds, st["n"], args.steps)
         if args.all_ranks:
             line["rank_balance"] = {mode: rank_balance(wl, torch, ds, dev, args, mode)
                                     for mode in ("round-robin", "in-seq")}

@@ -17,7 +17,7 @@ and fails loudly if the library has not been built.
 from ._lib import (  # noqa: F401
     DS32CPError, DS_BF16, DS_F32, DS_FP8_E4M3FN, DS_FP8_E4M3FN_ROWSCALE, LIB_PATH, abi_version,
     cp_in_seq_local_count, cp_local_count, cp_split_metadata, cp_split_metadata_in_seq,
-    decode_metadata, indexer_scores,
+    decode_metadata, gemm_bf16_nt, gemm_bf16_nt_workspace_size, indexer_scores,
     indexer_topk, indexer_topk_workspace_size, kv_cache_write, kv_cache_write_fp8, kv_rerange,
     sparse_mla_decode,
     sparse_mla_decode_noalloc,

@@ -69,6 +69,9 @@ _SIGS = {
     "sparse_mla_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
     "sparse_mla_decode": ([_p, _i32, _p, _i32, _p, _i64, _p, _i32, _i32, _i32, _i32,
                            _i32, _f32, _p, _i32, _p, _p, _sz, _p], _i32),
+    "gemm_bf16_nt_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
+    "gemm_bf16_nt": ([_p, _i64, _i64, _p, _i64, _i64, _p, _i32, _i64, _i64, _i32, _i32, _i32,
+                      _i32, _p, _sz, _p], _i32),
     "sparse_mla_decode_noalloc_scratch_bytes": ([], _sz),
     "sparse_mla_decode_noalloc": ([_p, _i32, _p, _i32, _p, _i64, _p, _i32, _i32, _i32, _i32,
                                    _i32, _f32, _p, _i32, _p, _p], _i32),
@@ -409,6 +412,53 @@ def sparse_mla_decode_noalloc(q, kv, topk_idx, sm_scale: float, d_latent: int, *
         dtype_code(out), _ptr(lse), _stream(stream))
     _check("sparse_mla_decode_noalloc", st)
     return out, lse
+
+
+def _gemm_operand(t: torch.Tensor, name: str):
+    """(pointer, rows, cols, leading dim, batch, batch stride) of a 2-d
+    [rows, cols] or 3-d [batch, rows, cols] view whose last dim is dense."""
+    if t.dim() == 2:
+        t3 = t.unsqueeze(0)
+    elif t.dim() == 3:
+        t3 = t
+    else:
+        raise ValueError(f"{name} must be 2-d or 3-d")
+    if t3.shape[2] > 1 and t3.stride(2) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    batch_stride = t3.stride(0) if t3.shape[0] > 1 else 0
+    return t3.data_ptr(), t3.shape[1], t3.shape[2], t3.stride(1), t3.shape[0], batch_stride
+
+
+def gemm_bf16_nt_workspace_size(M: int, N: int, K: int, batch: int = 1) -> int:
+    return lib.gemm_bf16_nt_workspace_size(M, N, K, batch)
+
+
+def gemm_bf16_nt(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+                 out_dtype=torch.bfloat16, workspace=None, stream=None) -> torch.Tensor:
+    """C = A . B^T per batch: a [.., M, K], b [.., N, K] (weights as
+    [out, in]), out [.., M, N]; 2-d or 3-d views whose last dimension is
+    dense (strided per-head slices are passed in place)."""
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise TypeError("a and b must be bf16")
+    pa, M, K, lda, ba, sa = _gemm_operand(a, "a")
+    pb, N, Kb, ldb, bb, sb = _gemm_operand(b, "b")
+    batch = max(ba, bb)
+    if Kb != K or ba not in (1, batch) or bb not in (1, batch):
+        raise ValueError("a [.., M, K] and b [.., N, K] must agree in K and batch")
+    if out is None:
+        shape = (batch, M, N) if a.dim() == 3 or b.dim() == 3 else (M, N)
+        out = torch.empty(shape, dtype=out_dtype, device=a.device)
+    pc, Mc, Nc, ldc, bc, scs = _gemm_operand(out, "out")
+    if (Mc, Nc) != (M, N) or bc not in (1, batch):
+        raise ValueError("out must be [.., M, N]")
+    need = gemm_bf16_nt_workspace_size(M, N, K, batch)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    st = lib.gemm_bf16_nt(pa, lda, sa, pb, ldb, sb, pc, dtype_code(out), ldc, scs, M, N, K,
+                          batch, _ptr(workspace) if need else None,
+                          workspace.numel() if need else 0, _stream(stream))
+    _check("gemm_bf16_nt", st)
+    return out
 
 
 def decode_metadata(lengths: torch.Tensor, out: dict | None = None, stream=None) -> dict:

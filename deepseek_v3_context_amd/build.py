@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libds32cp.so")
-SOURCES = ["api.hip", "split_rerange.hip", "indexer.hip", "topk.hip", "sparse_mla.hip"]
+SOURCES = ["api.hip", "split_rerange.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "gemm.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

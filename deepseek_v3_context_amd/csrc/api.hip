@@ -469,6 +469,40 @@ ds_status sparse_mla_decode(const void* q, ds_dtype q_dtype, const void* kv,
   return launch_sparse_mla(a, stream);
 }
 
+size_t gemm_bf16_nt_workspace_size(int32_t M, int32_t N, int32_t K, int32_t batch) {
+  if (M <= 0 || N <= 0 || K <= 0 || batch <= 0) return 0;
+  const int32_t splits = gemm_splits(M, N, K, batch);
+  return splits > 1 ? sizeof(float) * static_cast<size_t>(splits) * batch * M * N : 0;
+}
+
+ds_status gemm_bf16_nt(const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb,
+                       int64_t stride_b, void* C, ds_dtype c_dtype, int64_t ldc, int64_t stride_c,
+                       int32_t M, int32_t N, int32_t K, int32_t batch, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  const char* f = "gemm_bf16_nt";
+  DS_REQUIRE(M >= 0 && N >= 0 && K >= 0 && batch >= 0, DS_ERR_INVALID_ARG,
+             std::string(f) + ": negative size");
+  DS_REQUIRE(c_dtype == DS_BF16 || c_dtype == DS_F32, DS_ERR_UNSUPPORTED,
+             std::string(f) + ": C must be bf16 or f32");
+  DS_REQUIRE(K % 64 == 0 && N % 128 == 0, DS_ERR_UNSUPPORTED,
+             std::string(f) + ": K must be a multiple of 64 and N of 128");
+  if (static_cast<int64_t>(M) * N * batch == 0) return DS_OK;
+  DS_REQUIRE(A != nullptr && B != nullptr && C != nullptr, DS_ERR_INVALID_ARG,
+             std::string(f) + ": NULL operand");
+  DS_REQUIRE(lda >= K && ldb >= K && ldc >= N && stride_a >= 0 && stride_b >= 0 && stride_c >= 0,
+             DS_ERR_INVALID_ARG, std::string(f) + ": leading dimensions below the row length");
+  DS_REQUIRE(((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0 &&
+                 (lda | ldb | stride_a | stride_b) % 8 == 0,
+             DS_ERR_INVALID_ARG,
+             std::string(f) + ": A and B need 16-byte aligned rows (pointers, strides % 8)");
+  GemmArgs g{A, B, C, ws, lda, ldb, ldc, stride_a, stride_b, stride_c, M, N, K, batch, 1, c_dtype};
+  g.splits = gemm_splits(M, N, K, batch);
+  if (g.splits > 1)
+    DS_REQUIRE(ws != nullptr && ws_bytes >= gemm_bf16_nt_workspace_size(M, N, K, batch),
+               DS_ERR_WORKSPACE, std::string(f) + ": workspace smaller than gemm_bf16_nt_workspace_size()");
+  return launch_gemm(g, stream);
+}
+
 size_t sparse_mla_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 ds_status sparse_mla_decode_noalloc(const void* q, ds_dtype q_dtype, const void* kv,

@@ -193,6 +193,20 @@ struct MlaArgs {
   int32_t scale_shift = 7;   // fp8 kv: scale of row r is kv_scale[r >> scale_shift]
 };
 ds_status launch_sparse_mla(const MlaArgs& a, hipStream_t s);
+
+// Batched C = A . B^T (the projections); strides in elements.
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  void* ws;                       // split-K partials (fp32), splits > 1
+  int64_t lda, ldb, ldc;
+  int64_t strideA, strideB, strideC;
+  int32_t M, N, K, batch, splits;
+  ds_dtype c_dtype;
+};
+int32_t gemm_splits(int32_t M, int32_t N, int32_t K, int32_t batch);
+ds_status launch_gemm(GemmArgs g, hipStream_t s);
 size_t mla_partials_bytes(int32_t n_q, int32_t n_heads, int32_t d_latent,
                           int32_t n_splits);
 int32_t mla_decode_splits(int32_t n_q, int32_t topk);

@@ -1,0 +1,246 @@
+// The dense projections on either side of the path, as one batched GEMM.
+//
+// Sources: "Model Parallel Strategy Analysis", step 3.1 (MLA's projection
+// structure: q_down / q_up / kv_down / kv_up (K and V) / o_proj);
+// "[RFC]: Parallel strategy for Deepseek v3.2 like models", "Problem with
+// tp" (the indexer's wq_b and w_k projections, which every rank would
+// otherwise run on every token).  With the latent (absorbed) attention the
+// up-projection of K folds into the queries (q_latent = q_nope . W_UK per
+// head) and that of V into the output (o = O_latent . W_UV per head); both
+// are batched over the heads.
+//
+//   C[b][m][n] = sum_k A[b][m][k] * B[b][n][k]      (fp32 accumulation)
+//
+// A is M x K and B is N x K, both K-contiguous (weights stored as
+// [out, in]), C is M x N; every operand has its own row and batch stride,
+// so a per-head slice of a wider row (q_nope inside the q row, the latent
+// part of the 576-wide MLA query) is addressed in place.
+//
+// Kernel: 8 waves per workgroup (two per SIMD), a BM x BN output tile, K in
+// steps of 64.  Each step's A and B tiles (rows of 128 bytes) are copied
+// into LDS by direct global->LDS loads, double-buffered so that the next
+// step's copy runs under this step's products.  Within a tile row the
+// eight 16-byte chunks are stored XOR-permuted by bits 2..3 of the row, so
+// that the sixteen rows a 16-lane group reads for one MFMA fragment land in
+// sixteen distinct 16-byte bank slots.  Products: v_mfma_f32_32x32x16_bf16,
+// each wave a (BM/WM) x (BN/WN) sub-tile held in accumulator registers.
+// Split-K (few output tiles, long K): each split writes its fp32 partial
+// tile to the workspace and a second kernel sums the splits in order.
+#include "common.h"
+
+namespace ds32cp {
+
+namespace {
+
+constexpr int kGemmBK = 64;                 // K per step (128 bytes of a row)
+constexpr int kGemmThreads = 512;           // 8 waves
+
+// LDS byte offset of 16-byte chunk c of tile row r.
+__device__ __forceinline__ int gemm_lds_off(int r, int c) {
+  return (r << 7) | ((c ^ ((r >> 2) & 3)) << 4);
+}
+
+// One direct global->LDS copy of 16 bytes per lane: lane l lands at
+// lds + 16 l (lds: the instruction's block start, the same for the wave).
+__device__ __forceinline__ void gemm_dma(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      (size_t)((__attribute__((address_space(3))) const uint8_t*)p));
+}
+
+}  // namespace
+
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_nt_kernel(GemmArgs g, int32_t tiles_m, int32_t tiles_n, int32_t k_per_split) {
+  static_assert(WM * WN == kGemmThreads / kWave, "eight waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN;     // wave sub-tile
+  constexpr int FM = WTM / 32, FN = WTN / 32;     // 32 x 32 blocks per wave
+  constexpr int A_BYTES = BM * kGemmBK * 2, B_BYTES = BN * kGemmBK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_INST = A_BYTES / (kGemmThreads * 16);   // copies per thread and step
+  constexpr int B_INST = B_BYTES / (kGemmThreads * 16);
+  static_assert(A_INST >= 1 && B_INST >= 1, "a tile is at least one copy per thread");
+  __shared__ __align__(16) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+
+  // workgroup -> (batch, split, tile): consecutive logical ids share an A
+  // row block (N tiles vary fastest) and run on one XCD, whose L2 then
+  // serves that block to all of them
+  int64_t id = (gridDim.x & 7u) == 0 ? xcd_contiguous_id(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int32_t tn = static_cast<int32_t>(id % tiles_n);
+  id /= tiles_n;
+  const int32_t tm = static_cast<int32_t>(id % tiles_m);
+  id /= tiles_m;
+  const int32_t split = static_cast<int32_t>(id % g.splits);
+  const int32_t b = static_cast<int32_t>(id / g.splits);
+  const int32_t m0 = tm * BM, n0 = tn * BN;
+  const int32_t k_begin = split * k_per_split;
+  const int32_t k_steps = (min(g.K, k_begin + k_per_split) - k_begin) / kGemmBK;
+
+  const uint8_t* A = static_cast<const uint8_t*>(g.A) + (b * g.strideA + k_begin) * 2;
+  const uint8_t* B = static_cast<const uint8_t*>(g.B) + (b * g.strideB + k_begin) * 2;
+  // per-lane source of each copy: LDS chunk q = i*512 + tid holds row q/8,
+  // stored chunk q%8, i.e. global chunk (q%8) ^ ((row >> 2) & 3); rows past
+  // M (N) read the last valid row, whose products are never stored
+  const uint8_t* a_src[A_INST];
+  const uint8_t* b_src[B_INST];
+#pragma unroll
+  for (int i = 0; i < A_INST; ++i) {
+    const int q = i * kGemmThreads + tid, r = q >> 3;
+    const int gc = (q & 7) ^ ((r >> 2) & 3);
+    const int64_t row = min(m0 + r, g.M - 1);
+    a_src[i] = A + row * g.lda * 2 + gc * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < B_INST; ++i) {
+    const int q = i * kGemmThreads + tid, r = q >> 3;
+    const int gc = (q & 7) ^ ((r >> 2) & 3);
+    const int64_t row = min(n0 + r, g.N - 1);
+    b_src[i] = B + row * g.ldb * 2 + gc * 16;
+  }
+  const uint32_t s0 = lds_addr(smem);
+  auto issue = [&](int stage, int kt) {
+    const uint32_t base = s0 + stage * STAGE;
+    const int64_t koff = static_cast<int64_t>(kt) * kGemmBK * 2;
+#pragma unroll
+    for (int i = 0; i < A_INST; ++i)
+      gemm_dma(a_src[i] + koff, base + (i * kGemmThreads + wave * kWave) * 16);
+#pragma unroll
+    for (int i = 0; i < B_INST; ++i)
+      gemm_dma(b_src[i] + koff, base + A_BYTES + (i * kGemmThreads + wave * kWave) * 16);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // fragment offsets: lane l reads row (l % 32) of a 32-row block and
+  // chunk 2 kk + l / 32 for k-substep kk
+  const int fr = lane & 31, fh = lane >> 5;
+  if (k_steps > 0) issue(0, 0);
+  for (int kt = 0; kt < k_steps; ++kt) {
+    const int st = kt & 1;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of step kt landed
+    __syncthreads();                 // everyone's; and step kt-1's reads are done
+    if (kt + 1 < k_steps) issue(st ^ 1, kt + 1);
+    const uint8_t* sa = smem + st * STAGE;
+    const uint8_t* sb = sa + A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < kGemmBK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 32 + fr;
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + gemm_lds_off(r, 2 * kk + fh));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WTN + j * 32 + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + gemm_lds_off(r, 2 * kk + fh));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: lane l holds column l % 32 of each block, rows
+  // 8 (e / 4) + 4 (l / 32) + e % 4
+  const bool partial = g.splits > 1;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int32_t col = n0 + wn * WTN + j * 32 + fr;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int32_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+        if (row >= g.M) continue;
+        const float v = acc[i][j][e];
+        if (partial) {
+          float* p = static_cast<float*>(g.ws) +
+                     ((static_cast<int64_t>(split) * g.batch + b) * g.M + row) * g.N + col;
+          *p = v;
+        } else if (g.c_dtype == DS_BF16) {
+          uint16_t* c = static_cast<uint16_t*>(g.C) + b * g.strideC + static_cast<int64_t>(row) * g.ldc + col;
+          *c = f32_to_bf16_bits(v);
+        } else {
+          float* c = static_cast<float*>(g.C) + b * g.strideC + static_cast<int64_t>(row) * g.ldc + col;
+          *c = v;
+        }
+      }
+    }
+}
+
+// Sum of the split partials, in split order, then the output conversion.
+__global__ void __launch_bounds__(256)
+gemm_splitk_reduce_kernel(GemmArgs g) {
+  const int64_t total = static_cast<int64_t>(g.batch) * g.M * g.N;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const float* ws = static_cast<const float*>(g.ws);
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += stride) {
+    float s = 0.f;
+    for (int32_t k = 0; k < g.splits; ++k) s += ws[k * total + e];
+    const int64_t n = e % g.N, t = e / g.N, m = t % g.M, b = t / g.M;
+    const int64_t off = b * g.strideC + m * g.ldc + n;
+    if (g.c_dtype == DS_BF16) static_cast<uint16_t*>(g.C)[off] = f32_to_bf16_bits(s);
+    else static_cast<float*>(g.C)[off] = s;
+  }
+}
+
+int32_t gemm_splits(int32_t M, int32_t N, int32_t K, int32_t batch) {
+  const int64_t bn = N % 256 == 0 ? 256 : 128;
+  const int64_t tiles = ceil_div(M, 256) * (N / bn) * static_cast<int64_t>(batch);
+  const int64_t cus = device_cu_count();
+  const int64_t steps = K / kGemmBK;
+  if (tiles >= cus || steps < 16) return 1;
+  int64_t s = ceil_div(2 * cus, tiles);
+  s = s < steps / 8 ? s : steps / 8;        // at least 8 steps per split
+  s = s < 16 ? s : 16;
+  return static_cast<int32_t>(s > 1 ? s : 1);
+}
+
+ds_status launch_gemm(GemmArgs g, hipStream_t s) {
+  if (g.M == 0 || g.N == 0 || g.batch == 0) return DS_OK;
+  const int32_t k_steps = g.K / kGemmBK;
+  const int32_t per = static_cast<int32_t>(ceil_div(k_steps, g.splits)) * kGemmBK;
+  const int32_t tiles_m = static_cast<int32_t>(ceil_div(g.M, 256));
+  if (g.N % 256 == 0) {
+    const int32_t tiles_n = g.N / 256;
+    const int64_t blocks = static_cast<int64_t>(tiles_m) * tiles_n * g.splits * g.batch;
+    gemm_nt_kernel<256, 256, 2, 4><<<static_cast<unsigned>(blocks), kGemmThreads, 0, s>>>(
+        g, tiles_m, tiles_n, per);
+  } else {
+    const int32_t tiles_n = g.N / 128;
+    const int64_t blocks = static_cast<int64_t>(tiles_m) * tiles_n * g.splits * g.batch;
+    gemm_nt_kernel<256, 128, 4, 2><<<static_cast<unsigned>(blocks), kGemmThreads, 0, s>>>(
+        g, tiles_m, tiles_n, per);
+  }
+  ds_status st = check_launch("gemm_bf16_nt");
+  if (st != DS_OK || g.splits == 1) return st;
+  const int64_t total = static_cast<int64_t>(g.batch) * g.M * g.N;
+  const int64_t want = ceil_div(total, 256);
+  gemm_splitk_reduce_kernel<<<static_cast<unsigned>(want < 16384 ? want : 16384), 256, 0, s>>>(g);
+  return check_launch("gemm_bf16_nt (split-K sum)");
+}
+
+}  // namespace ds32cp

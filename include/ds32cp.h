@@ -318,6 +318,35 @@ ds_status sparse_mla_decode(const void* q, ds_dtype q_dtype, const void* kv,
                             void* out, ds_dtype out_dtype, float* lse,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------
+ * The dense projections on either side of the path.  [ASCEND] step 3.1
+ * (MLA's q_down / q_up / kv_down / kv_up (K, V) / o_proj projections);
+ * [RFC] "Problem with tp" (the indexer's wq_b and w_k, run by every rank on
+ * every token under tensor parallelism; here each rank runs them on its
+ * own tokens).  With the latent attention the K up-projection folds into
+ * the queries (q_latent[h] = q_nope[h] . W_UK[h]) and the V up-projection
+ * into the output (o[h] = O_latent[h] . W_UV[h]); both are batched over
+ * the heads.  One batched GEMM serves all of them:
+ *     C[b][m][n] = sum_k A[b][m][k] * B[b][n][k]       (fp32 accumulation)
+ *   A  bf16, row m of batch b at A + b*stride_a + m*lda (K values, contiguous)
+ *   B  bf16, row n of batch b at B + b*stride_b + n*ldb (weights as [out, in])
+ *   C  bf16 (round to nearest even) or f32, C + b*stride_c + m*ldc + n
+ *   strides and leading dimensions in elements; per-head slices of wider
+ *   rows are addressed in place (e.g. the latent part of a 576-wide row)
+ *   ws  split-K partials, gemm_bf16_nt_workspace_size() bytes (0: none)
+ * Supported: K a multiple of 64, N a multiple of 128, A and B 16-byte
+ * aligned with lda, ldb, stride_a, stride_b multiples of 8.  C must not
+ * overlap A or B.
+ * Errors: INVALID_ARG (negative sizes, NULL operands, lda < K, ldb < K,
+ * ldc < N, misalignment), UNSUPPORTED (K, N or C dtype), WORKSPACE.
+ * ------------------------------------------------------------------- */
+size_t gemm_bf16_nt_workspace_size(int32_t M, int32_t N, int32_t K, int32_t batch);
+
+ds_status gemm_bf16_nt(const void* A, int64_t lda, int64_t stride_a, const void* B,
+                       int64_t ldb, int64_t stride_b, void* C, ds_dtype c_dtype,
+                       int64_t ldc, int64_t stride_c, int32_t M, int32_t N, int32_t K,
+                       int32_t batch, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Allocation-free variant of sparse_mla_decode, for callers that cannot
  * allocate device memory or pass a workspace (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  Same arguments
