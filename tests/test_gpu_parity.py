@@ -398,7 +398,13 @@ def test_topk_rows_longer_than_the_cache():
     r3[rng.choice(L, 2000, replace=False)] = 4.0                           # ... 2000 above: bucket > cache
     rows.append(r3)
     rows.append(rng.standard_normal(L).astype(np.float32))                 # short row (select all)
-    lens = np.array([L, L, L, 36000, 1000], dtype=np.int32)
+    # every 20th position low (a strided pattern), and a clustered row
+    r5 = rng.standard_normal(L).astype(np.float32)
+    r5[(np.arange(2048) * L + L // 2) // 2048] = -5.0
+    rows.append(r5)
+    r6 = rng.standard_normal(30000).astype(np.float32) * 1e-3 + 7.0       # clustered, in the cache
+    rows.append(np.concatenate([r6, np.zeros(L - 30000, np.float32)]))
+    lens = np.array([L, L, L, 36000, 1000, L, 30000], dtype=np.int32)
     scores = np.full((len(rows), L), np.nan, dtype=np.float32)
     for i, r in enumerate(rows):
         scores[i, : lens[i]] = r[: lens[i]]
