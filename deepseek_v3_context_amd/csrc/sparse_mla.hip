@@ -427,6 +427,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // exact in fp32/bf16 range terms) makes the workgroup start over with the
 // exact maximum from a first pass over all its rows.
 constexpr float kWideBail = 64.f;
+// QK steps before the end of a tile's QK at which the lagged loop issues the
+// LDS reads of the PV products that follow (their latency then overlaps the
+// last QK products)
+constexpr int kHookSteps = 4;
 
 // QK products with the accumulator in VGPRs (the compiler gives every MFMA
 // of a function the same accumulator file, and O^T fills the accumulator
@@ -647,8 +651,12 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
 
   // S^T = K Q^T of the tile in buf for heads h0, h0+16 (2 key blocks x 2
   // head blocks), optionally issuing this wave's gather slots of another
-  // tile (rows sidx[t0g..], into gbuf) spread over the k-steps
-  auto qk = [&](const uint8_t* tile, f32x4 (&st)[2][2], bool gather, int t0g, int gb) {
+  // tile (rows sidx[t0g..], into gbuf) spread over the k-steps.  `hook`
+  // runs after the products of step kMlaKSteps - kHookSteps: the lagged
+  // loop issues there the LDS reads of the PV products that follow, so
+  // that their latency is spent under the last QK products.
+  auto qk = [&](const uint8_t* tile, f32x4 (&st)[2][2], bool gather, int t0g, int gb,
+                auto&& hook) __attribute__((always_inline)) {
     // the gather's row is read first, so that waiting for it does not wait
     // for the K fragment reads behind it
     const uint8_t* gsrc = gather ? row_of(t0g) : kv;
@@ -659,54 +667,64 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       return __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const uint4*>(tile + koff + kb * 256 + ks * 2048));
     };
-    f32x4 su[2][2];
-    // K fragments are read kAhead k-steps before their products; the
+    // step s multiplies k-step ks_of(s): the two rope k-steps first, whose
+    // Q^T fragments come from LDS and are read here with the first K
+    // fragments, then the latent ones (Q^T in VGPRs)
+    auto ks_of = [](int s) { return s < 2 ? kQReg + s : s - 2; };
+    bf16x8 qr[2][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        qr[r][hb] = __builtin_bit_cast(bf16x8, sh.qrope[r][grp][h0 + 16 * hb]);
+    // K fragments are read kAhead steps before their products; the
     // scheduling barriers keep the compiler from sinking the reads next to
     // their use (one wave per SIMD: nothing else hides the LDS latency)
     constexpr int kAhead = 2;
-    // k-steps over which the gather slots are spread: the lagged schedule
+    // steps over which the gather slots are spread: the lagged schedule
     // gathers only one tile ahead, so its slots go out in the first half
     constexpr int kSpread = kLag ? kMlaKSteps / 2 : kMlaKSteps;
     bf16x8 kf[kAhead + 1][2];
 #pragma unroll
     for (int s = 0; s < kAhead; ++s) {
-      kf[s][0] = kfrag(0, s);
-      kf[s][1] = kfrag(1, s);
+      kf[s][0] = kfrag(0, ks_of(s));
+      kf[s][1] = kfrag(1, ks_of(s));
     }
 #pragma unroll
-    for (int ks = 0; ks < kMlaKSteps; ++ks) {
+    for (int s = 0; s < kMlaKSteps; ++s) {
       __builtin_amdgcn_sched_barrier(0);
-      if (ks + kAhead < kMlaKSteps) {
-        kf[(ks + kAhead) % (kAhead + 1)][0] = kfrag(0, ks + kAhead);
-        kf[(ks + kAhead) % (kAhead + 1)][1] = kfrag(1, ks + kAhead);
+      if (s + kAhead < kMlaKSteps) {
+        kf[(s + kAhead) % (kAhead + 1)][0] = kfrag(0, ks_of(s + kAhead));
+        kf[(s + kAhead) % (kAhead + 1)][1] = kfrag(1, ks_of(s + kAhead));
       }
-      const bf16x8 k0 = kf[ks % (kAhead + 1)][0], k1 = kf[ks % (kAhead + 1)][1];
+      // the reads go out before this step's products, not after them
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 k0 = kf[s % (kAhead + 1)][0], k1 = kf[s % (kAhead + 1)][1];
+      const int ks = ks_of(s);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        const bf16x8 qv = ks < kQReg ? qf[hb][ks < kQReg ? ks : 0]
-                                     : __builtin_bit_cast(bf16x8, sh.qrope[ks - kQReg][grp][h0 + 16 * hb]);
-        // even and odd k-steps accumulate separately: 8 independent chains
-        f32x4 (&acc)[2][2] = (ks & 1) ? su : st;
-        if (ks < 2) {
-          acc[0][hb] = mla_qk_first(k0, qv);
-          acc[1][hb] = mla_qk_first(k1, qv);
+        const bf16x8 qv = ks < kQReg ? qf[hb][ks < kQReg ? ks : 0] : qr[ks - kQReg][hb];
+        // four independent chains (key block x head block)
+        if (s == 0) {
+          st[0][hb] = mla_qk_first(k0, qv);
+          st[1][hb] = mla_qk_first(k1, qv);
         } else {
-          mla_qk_acc(acc[0][hb], k0, qv);
-          mla_qk_acc(acc[1][hb], k1, qv);
+          mla_qk_acc(st[0][hb], k0, qv);
+          mla_qk_acc(st[1][hb], k1, qv);
         }
       }
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        if (i * kSpread / kPer == ks && gather) wide_gather_issue(gsrc + 32 * kNW * i, slot_lds(gb, i));
+        if (i * kSpread / kPer == s && gather) wide_gather_issue(gsrc + 32 * kNW * i, slot_lds(gb, i));
+      }
+      if (s == kMlaKSteps - kHookSteps) {
+        __builtin_amdgcn_sched_barrier(0);
+        hook();
       }
     }
     mla_qk_settle(st[0][0], st[0][1], st[1][0], st[1][1]);
-    mla_qk_settle(su[0][0], su[0][1], su[1][0], su[1][1]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) st[kb][hb] += su[kb][hb];
   };
+  auto no_hook = []() __attribute__((always_inline)) {};
   // scaled logits, masked: st[kb][hb][i] is key 16kb + 4grp + i, head h0+16hb
   auto logits = [&](f32x4 (&st)[2][2], uint64_t valid, float (&mx)[2]) {
 #pragma unroll
@@ -738,41 +756,47 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   // interleave has to be one product at a time: unit u (of 64) is a small
   // piece of softmax followed by one PV product, with scheduling barriers
   // between them so that the compiler keeps that order.
-  //   pv_c: issue the PV products of the previous tile (V in vtile, P^T in
+  //   pv_c: issue the PV products of the previous tile (its V^T fragments
+  //         in vf and the P^T fragments of head groups 0 and 1 in pf, read
+  //         by pv_reads; the later groups are read two groups ahead from
   //         parity buffer pb_rd); sm_c: run the softmax of st and write its
   //         P^T to parity buffer pb_wr.  Softmax without PV is the first
   //         tile, which also sets the reference maximum.
-  auto phase_b = [&](auto pv_c, auto sm_c, const uint8_t* vtile, int pb_rd, int pb_wr,
-                     f32x4 (&st)[2][2], bool& beyond) __attribute__((always_inline)) {
+  constexpr int kCBL = kCB < 8 ? kCB : 8;   // column blocks whose V fragments are held
+  bf16x8 vf[kCBL];
+  bf16x8 pf[3];
+  auto load_p = [&](int pb, int hg) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    return __builtin_bit_cast(bf16x8, sh.p[pb][ln >> 4][hg * 16 + (ln & 15)]);
+  };
+  // the LDS reads the PV products of a tile start with: its V^T fragments
+  // (transposed reads of the tile in vtile) and P^T of head groups 0 and 1
+  auto pv_reads = [&](const uint8_t* vtile, int pb) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int voff = wide_voff(ln, wave * kCols);
+#pragma unroll
+    for (int c = 0; c < kCBL; ++c) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vtile + voff + c * 1024));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vtile + voff + 256 + c * 1024));
+      vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    pf[0] = load_p(pb, 0);
+    pf[1] = load_p(pb, 1);
+  };
+  auto phase_b = [&](auto pv_c, auto sm_c, int pb_rd, int pb_wr, f32x4 (&st)[2][2],
+                     bool& beyond) __attribute__((always_inline)) {
     constexpr bool kPV = decltype(pv_c)::value;
     constexpr bool kSM = decltype(sm_c)::value;
     constexpr bool kFirst = !kPV;
-    constexpr int kCBL = kCB < 8 ? kCB : 8;   // column blocks whose V fragments are held
     constexpr int kUnits = kCB * kHG;         // PV products per tile and wave
     static_assert(kUnits == 64, "64 PV products per tile and wave");
     static_assert(kCB == kCBL, "the lagged schedule holds every V fragment of the wave");
     float mx[2], nm[2], psum[2] = {0.f, 0.f};
     bf16x8 pvb[2];
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int li_t = ln & 15, grp_t = ln >> 4;
-    const int voff = wide_voff(ln, wave * kCols);
-    bf16x8 vf[kCBL];
-    bf16x8 pf[2];
-    auto load_p = [&](int hg) {
-      return __builtin_bit_cast(bf16x8, sh.p[pb_rd][grp_t][hg * 16 + li_t]);
-    };
-    if constexpr (kPV) {
-#pragma unroll
-      for (int c = 0; c < kCBL; ++c) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vtile + voff + c * 1024));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vtile + voff + 256 + c * 1024));
-        vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-      pf[0] = load_p(0);
-    }
     // softmax pieces; u is a compile-time constant once the unit loop is
     // unrolled.  Values: st[kb][hb][i] is key 16kb + 4grp + i of head
     // h0 + 16hb; v = 8hb + 4kb + i.
@@ -846,9 +870,9 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kPV) {
         constexpr int hg = u / kCBL, c = u % kCBL;
-        // the next head group's P^T fragment, read one group ahead
-        if constexpr (c == 0 && hg + 1 < kHG) pf[(hg + 1) & 1] = load_p(hg + 1);
-        o[c][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c], pf[hg & 1], o[c][hg], 0, 0, 0);
+        // P^T fragments are read two head groups ahead
+        if constexpr (c == 0 && hg + 2 < kHG) pf[(hg + 2) % 3] = load_p(pb_rd, hg + 2);
+        o[c][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c], pf[hg % 3], o[c][hg], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -867,7 +891,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
         __syncthreads();
         const uint64_t valid = tile_valid_mask(n_valid - t * kPipeTile);
         f32x4 st[2][2];
-        qk(g_mla_bufs, st, false, 0, 0);
+        qk(g_mla_bufs, st, false, 0, 0, no_hook);
         float mx[2];
         logits(st, valid, mx);
         m_ref[0] = fmaxf(m_ref[0], mx[0]);
@@ -891,12 +915,12 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       const std::true_type yes{};
       const std::false_type no{};
       // QK of tile t (buffer b) with the gather of tile t+1 spread through it
-      auto qk_tile = [&](int32_t t, int b, f32x4 (&st)[2][2]) __attribute__((always_inline)) {
+      auto qk_tile = [&](int32_t t, int b, f32x4 (&st)[2][2], auto&& hook) __attribute__((always_inline)) {
         const uint8_t* tile = g_mla_bufs + b * kPipeTileBytes;
         // the gather of tile t+1 is issued unconditionally (after the last
         // tile it reads padding rows into a free buffer), so the k-step loop
         // has no branch; the epilogue waits for it before reusing the buffers
-        qk(tile, st, true, (t + 1) * kPipeTile, b == 2 ? 0 : b + 1);
+        qk(tile, st, true, (t + 1) * kPipeTile, b == 2 ? 0 : b + 1, hook);
         // valid rows are compacted to the front: only the last tile is
         // partial; its missing keys get a logit of -inf (weight 0)
         const int32_t rem = n_valid - t * kPipeTile;
@@ -920,9 +944,9 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       if (n_tiles > 0) {
         tile_barrier();
         f32x4 st[2][2];
-        qk_tile(0, 0, st);
+        qk_tile(0, 0, st, no_hook);
         bool beyond = false;
-        phase_b(no, yes, g_mla_bufs, 0, 0, st, beyond);
+        phase_b(no, yes, 0, 0, st, beyond);
       }
       for (int32_t t = 1, b = 1; t < n_tiles; ++t, b = b == 2 ? 0 : b + 1) {
         tile_barrier();
@@ -934,10 +958,13 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
           break;
         }
         f32x4 st[2][2];
-        qk_tile(t, b, st);
+        // the PV reads of tile t-1 (buffer b-1, P^T parity (t-1) & 1) go out
+        // near the end of QK of tile t
+        const uint8_t* vtile = g_mla_bufs + (b == 0 ? 2 : b - 1) * kPipeTileBytes;
+        const int pb_rd = (t - 1) & 1;
+        qk_tile(t, b, st, [&]() __attribute__((always_inline)) { pv_reads(vtile, pb_rd); });
         bool beyond = false;
-        phase_b(yes, yes, g_mla_bufs + (b == 0 ? 2 : b - 1) * kPipeTileBytes,
-                (t - 1) & 1, t & 1, st, beyond);
+        phase_b(yes, yes, pb_rd, t & 1, st, beyond);
       }
       if (!bailed && n_tiles > 0) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -953,7 +980,8 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
           f32x4 st[2][2];
           bool beyond = false;
           const int bl = (n_tiles - 1) % 3;
-          phase_b(yes, no, g_mla_bufs + bl * kPipeTileBytes, (n_tiles - 1) & 1, 0, st, beyond);
+          pv_reads(g_mla_bufs + bl * kPipeTileBytes, (n_tiles - 1) & 1);
+          phase_b(yes, no, (n_tiles - 1) & 1, 0, st, beyond);
         }
       }
     } else
@@ -968,7 +996,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
       const uint64_t valid = tile_valid_mask(n_valid - t * kPipeTile);
       // ---- QK, with the gather of tile t+2 into the buffer of tile t-1
       f32x4 st[2][2];
-      qk(tile, st, t + 2 < n_tiles, (t + 2) * kPipeTile, b == 0 ? 2 : b - 1);
+      qk(tile, st, t + 2 < n_tiles, (t + 2) * kPipeTile, b == 0 ? 2 : b - 1, no_hook);
       // ---- softmax weights relative to the fixed reference
       float mx[2];
       logits(st, valid, mx);
@@ -1132,6 +1160,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
     }
   }
 }
+
 
 // Merge split partials: one workgroup per (query, 4 heads), 64 threads per
 // head, 8 output columns (one 16-byte load per split) per thread.
