@@ -8,14 +8,21 @@
 // causal keys select all of them and pad with -1.
 //
 // One workgroup per query row.  Scores are mapped to order-preserving
-// 32-bit keys and the k-th largest key is found by four 8-bit radix passes
-// (per-wave LDS histograms + one-wave suffix scan per pass).  Rows that fit
-// are cached in LDS so the passes never return to memory; longer rows are
-// staged through LDS block by block on every pass.  A final ordered pass
-// (block-wide scans) writes the selected positions in ascending order:
-// every key above the threshold and the lowest-position keys equal to it,
-// so the selected set is exactly the tie-to-lower-position set and the
-// output is deterministic.
+// 32-bit keys.  In launches for long rows, rows of up to 65536 keys take
+// the bitmap path: one read
+// of the row from memory (16-bit keys cached in LDS, a 4096-bin histogram of
+// the top 12 bits), a pass over the cache that records the keys above the
+// threshold bin in a bitmap of positions, an exact resolution of the
+// threshold bin's few keys, and one scan of the bitmap for the output.
+// Other rows (and rows whose threshold bin is too crowded) take the general
+// path: the k-th largest key is found by four 8-bit radix passes (per-wave
+// LDS histograms + one-wave suffix scan per pass); rows that fit are cached
+// in LDS so the passes never return to memory, longer rows are staged
+// through LDS block by block on every pass, and a final ordered pass
+// (block-wide scans) writes the selected positions.  Both write every key
+// above the threshold and the lowest-position keys equal to it, in
+// ascending position order, so the selected set is exactly the
+// tie-to-lower-position set and the output is deterministic.
 #include <mutex>
 
 #include "common.h"
@@ -24,6 +31,14 @@ namespace ds32cp {
 
 constexpr int kTkPer = 8;                 // consecutive keys per thread and step
 constexpr int32_t kTkCacheKeys = 32768;   // 128 KiB of LDS
+// Bitmap path: bins of the first digit (the top 12 bits of the 32-bit
+// key), the most threshold-bucket keys it resolves in LDS, and the longest
+// row it takes (16-bit keys in the cache; positions fit in 16 bits).  Only
+// the 1024-thread kernel (long rows) has it: the 512-thread one keeps its
+// smaller LDS footprint, and with it two or three workgroups per CU.
+constexpr int kTkBins = 4096;
+constexpr int kTkCandMax = 2048;
+constexpr int32_t kTkBitmapMaxLen = 65536;
 
 __device__ __forceinline__ int64_t topk_key_row(const TopkArgs& a, int32_t req,
                                                 int64_t l) {
@@ -63,6 +78,235 @@ __device__ __forceinline__ uint32_t tk_block_scan(uint32_t v, int lane, int wave
   return before + incl - v;
 }
 
+// Bitmap path of the single-workgroup selection (see topk_kernel).  Returns
+// false, having written nothing, when the threshold bin holds more than
+// kTkCandMax keys.  Uniform control flow: every thread takes every branch.
+template <int kTkThreads>
+__device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_scores,
+                            int32_t* out_idx, float* out_score, int32_t req, int64_t kv0,
+                            uint32_t* cache, uint32_t* hw, uint16_t* cand_pos,
+                            uint32_t* cand_key, uint32_t* wave_tot, uint32_t& sh_digit,
+                            uint32_t& sh_remaining, uint32_t& sh_count, uint32_t& sh_ncand) {
+  constexpr int kTkWaves = kTkThreads / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
+  const uint32_t k = static_cast<uint32_t>(a.topk);
+
+  // The digit of `bins` bins (a power of two, a multiple of kTkThreads)
+  // holding the `want`-th largest counted key: counts in hist[0..bins),
+  // thread t owns bins [(n-1-t)*per, (n-t)*per) so that thread order is
+  // descending bin order.  Sets sh_digit, sh_remaining (keys still wanted
+  // from that bin) and sh_count (the bin's count).
+  auto find_bin = [&](const uint32_t* hist, int bins, uint32_t want) {
+    const int per = bins / kTkThreads;
+    const int b0 = bins - per * (tid + 1);
+    uint32_t c = 0;
+    for (int i = 0; i < per; ++i) c += hist[b0 + i];
+    uint32_t total;
+    uint32_t cum = tk_block_scan<kTkWaves>(c, lane, wave, wave_tot, total);   // keys in higher bins
+    for (int i = per - 1; i >= 0; --i) {
+      const uint32_t ci = hist[b0 + i];
+      if (cum < want && cum + ci >= want) {
+        sh_digit = static_cast<uint32_t>(b0 + i);
+        sh_remaining = want - cum;
+        sh_count = ci;
+      }
+      cum += ci;
+    }
+    __syncthreads();
+  };
+
+  // ---- pass A: the row from memory, 4 keys per thread and load
+  for (int i = tid; i < kTkBins; i += kTkThreads) hw[i] = 0u;
+  __syncthreads();
+  const bool vec = (reinterpret_cast<uintptr_t>(row_scores) & 15u) == 0;
+  // 16 loads of 16 bytes in flight per thread: a row of 65536 keys in one
+  // round (this pass waits on memory, not on its arithmetic)
+  constexpr int kU = 16;
+  for (int32_t r0 = 0; r0 < L; r0 += 4 * kTkThreads * kU) {
+    float4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t t = r0 + 4 * (u * kTkThreads + tid);
+      if (vec && t + 4 <= L) {
+        v[u] = *reinterpret_cast<const float4*>(row_scores + t);
+      } else {
+        v[u].x = t < L ? row_scores[t] : 0.f;
+        v[u].y = t + 1 < L ? row_scores[t + 1] : 0.f;
+        v[u].z = t + 2 < L ? row_scores[t + 2] : 0.f;
+        v[u].w = t + 3 < L ? row_scores[t + 3] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t t = r0 + 4 * (u * kTkThreads + tid);
+      if (t >= L) continue;
+      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t key[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[e] = float_order_key(f[e]);
+      if (t + 4 <= L) {
+        *reinterpret_cast<uint2*>(c16 + t) =
+            make_uint2((key[0] >> 16) | (key[1] & 0xffff0000u), (key[2] >> 16) | (key[3] & 0xffff0000u));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (t + e < L) c16[t + e] = static_cast<uint16_t>(key[e] >> 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (t + e < L) atomicAdd(&hw[key[e] >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  find_bin(hw, kTkBins, k);
+  const uint32_t T = sh_digit;
+  uint32_t remaining = sh_remaining;   // keys still wanted from bin T
+  const uint32_t n_t = sh_count;
+  if (n_t > static_cast<uint32_t>(kTkCandMax)) return false;   // uniform
+
+  // ---- pass B: bitmap of keys in bins above T, positions of bin T.  The
+  // bitmap takes words [0, 2048) of hw (the histogram is consumed).
+  uint32_t* bm = hw;
+  uint32_t* aux = hw + 2048;   // radix histogram, then the tie bitmap
+  const int32_t n_words = (L + 31) >> 5;
+  if (tid == 0) sh_ncand = 0;
+  __syncthreads();
+  for (int32_t w0 = 0; w0 < n_words; w0 += kTkThreads) {
+    const int32_t w = w0 + tid;
+    uint32_t bits = 0, tbits = 0;
+    if (w < n_words) {
+      const int32_t p0 = w << 5;
+      if (p0 + 32 <= L) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 x = *reinterpret_cast<const uint4*>(c16 + p0 + 8 * q);
+          const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            const uint32_t b = ((wd[h >> 1] >> (16 * (h & 1))) & 0xffffu) >> 4;
+            bits |= (b > T ? 1u : 0u) << (8 * q + h);
+            tbits |= (b == T ? 1u : 0u) << (8 * q + h);
+          }
+        }
+      } else {
+        for (int e = 0; p0 + e < L; ++e) {
+          const uint32_t b = static_cast<uint32_t>(c16[p0 + e]) >> 4;
+          bits |= (b > T ? 1u : 0u) << e;
+          tbits |= (b == T ? 1u : 0u) << e;
+        }
+      }
+      bm[w] = bits;
+    }
+    // the bin's positions, appended wave by wave (their order is free)
+    const uint32_t nt = static_cast<uint32_t>(__popc(tbits));
+    uint32_t incl = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    uint32_t base = 0;
+    if (lane == 63 && incl > 0) base = atomicAdd(&sh_ncand, incl);
+    base = __shfl(base, 63) + incl - nt;
+    while (tbits) {
+      const int e = __builtin_ctz(tbits);
+      tbits &= tbits - 1u;
+      if (base < static_cast<uint32_t>(kTkCandMax)) cand_pos[base] = static_cast<uint16_t>((w << 5) + e);
+      ++base;
+    }
+  }
+  __syncthreads();
+  const int32_t n_c = static_cast<int32_t>(n_t);   // == sh_ncand: every key was counted once
+
+  // ---- the k-th largest key among bin T: full keys, two 10-bit passes
+  for (int32_t i = tid; i < n_c; i += kTkThreads)
+    cand_key[i] = float_order_key(row_scores[cand_pos[i]]);
+  uint32_t prefix = T << 20, mask = 0xfff00000u;
+  for (int shift = 10; shift >= 0; shift -= 10) {
+    for (int i = tid; i < 1024; i += kTkThreads) aux[i] = 0u;
+    __syncthreads();
+    for (int32_t i = tid; i < n_c; i += kTkThreads) {
+      const uint32_t u = cand_key[i];
+      if ((u & mask) == prefix) atomicAdd(&aux[(u >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin(aux, 1024, remaining);
+    prefix |= sh_digit << shift;
+    mask |= 1023u << shift;
+    remaining = sh_remaining;
+    __syncthreads();   // sh_* read by all before the next pass writes them
+  }
+  const uint32_t thr = prefix;           // the k-th largest key of the row
+  const uint32_t n_eq = sh_count;        // keys equal to it
+  const bool all_eq = remaining == n_eq; // every one of them is taken
+
+  // ---- keys of bin T above the threshold join the bitmap; equal keys go
+  // to the tie bitmap (aux), unless all of them are taken
+  for (int32_t i = tid; i < n_words; i += kTkThreads) aux[i] = 0u;
+  __syncthreads();
+  for (int32_t i = tid; i < n_c; i += kTkThreads) {
+    const uint32_t u = cand_key[i];
+    const uint32_t p = cand_pos[i];
+    if (u > thr || (u == thr && all_eq)) atomicOr(&bm[p >> 5], 1u << (p & 31u));
+    else if (u == thr) atomicOr(&aux[p >> 5], 1u << (p & 31u));
+  }
+  __syncthreads();
+  // thread t covers words [wpt*t, wpt*t + wpt): thread order is position order
+  constexpr int kWpt = 2048 / kTkThreads;
+  if (!all_eq) {   // uniform: the lowest `remaining` tied positions
+    uint32_t tw[kWpt], c = 0;
+#pragma unroll
+    for (int q = 0; q < kWpt; ++q) {
+      const int32_t w = kWpt * tid + q;
+      tw[q] = w < n_words ? aux[w] : 0u;
+      c += static_cast<uint32_t>(__popc(tw[q]));
+    }
+    uint32_t total;
+    uint32_t r = tk_block_scan<kTkWaves>(c, lane, wave, wave_tot, total);
+#pragma unroll
+    for (int q = 0; q < kWpt; ++q) {
+      uint32_t take = 0, x = tw[q];
+      while (x) {
+        const uint32_t bit = x & (0u - x);
+        x ^= bit;
+        if (r < remaining) take |= bit;
+        ++r;
+      }
+      if (take) atomicOr(&bm[kWpt * tid + q], take);
+    }
+    __syncthreads();
+  }
+
+  // ---- ascending positions of the selected keys, mapped to rows
+  uint32_t sw[kWpt], c = 0;
+#pragma unroll
+  for (int q = 0; q < kWpt; ++q) {
+    const int32_t w = kWpt * tid + q;
+    sw[q] = w < n_words ? bm[w] : 0u;
+    c += static_cast<uint32_t>(__popc(sw[q]));
+  }
+  uint32_t total;
+  uint32_t slot = tk_block_scan<kTkWaves>(c, lane, wave, wave_tot, total);
+#pragma unroll
+  for (int q = 0; q < kWpt; ++q) {
+    uint32_t x = sw[q];
+    while (x) {
+      const int e = __builtin_ctz(x);
+      x &= x - 1u;
+      const int32_t pos = ((kWpt * tid + q) << 5) + e;
+      if (slot < k) {
+        out_idx[slot] = static_cast<int32_t>(topk_key_row(a, req, kv0 + pos));
+        if (out_score) out_score[slot] = order_key_to_float(float_order_key(row_scores[pos]));
+      }
+      ++slot;
+    }
+  }
+  return true;
+}
+
 // kMode 0: one workgroup selects a whole row.
 // kMode 1 (two-phase, first phase): workgroup (row, s) selects the top-k of
 //   positions [s*seg_len, (s+1)*seg_len) of its row and writes them (score
@@ -78,11 +322,17 @@ template <int kTkThreads, int kMode>
 __global__ void __launch_bounds__(kTkThreads)
 topk_kernel(TopkArgs a, int32_t cache_keys) {
   constexpr int kTkWaves = kTkThreads / kWave;
+  constexpr bool kBitmap = kMode == 0 && kTkThreads == 1024;
   extern __shared__ __align__(16) uint32_t cache[];
-  __shared__ uint32_t hist[kTkWaves][256];   // one histogram per wave (less contention)
+  // one 256-bin histogram per wave (less contention); the bitmap path uses
+  // the same words as one 4096-bin histogram, then as its bitmaps
+  constexpr int kHistWords = kBitmap && kTkBins > kTkWaves * 256 ? kTkBins : kTkWaves * 256;
+  __shared__ uint32_t hist_words[kHistWords];
+  uint32_t (*hist)[256] = reinterpret_cast<uint32_t (*)[256]>(hist_words);
   __shared__ uint32_t sh_digit, sh_remaining, sh_count, sh_ncand;
   __shared__ uint32_t wave_tot[kTkWaves];
   __shared__ int32_t sel_t[kTopkMax];        // selected elements in output order (kMode 0, 2)
+  __shared__ uint16_t cand_pos[kBitmap ? kTkCandMax : 1];   // bitmap path: bucket positions
 
   const int32_t j = kMode == 1 ? static_cast<int32_t>(blockIdx.x / a.n_seg) : blockIdx.x;
   const int32_t seg = kMode == 1 ? static_cast<int32_t>(blockIdx.x % a.n_seg) : 0;
@@ -147,6 +397,27 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
       }
     }
     return;
+  }
+
+  // ---- bitmap path (rows of up to 65536 keys, 1024-thread kernel).  The row is read from
+  // memory once: every key's top 16 bits go to LDS and its top 12 bits are
+  // counted.  The bin holding the k-th largest key (the threshold bin) then
+  // splits the row: keys in higher bins are selected, and a pass over the
+  // cached keys records them in a bitmap of positions and lists the
+  // positions of the threshold bin.  Those (few) keys are read again in
+  // full and the k-th largest key is found among them by two 10-bit radix
+  // passes; keys above it join the bitmap, and of the keys equal to it the
+  // lowest positions are taken (their own bitmap, ranked by a scan).  One
+  // scan over the bitmap writes the selected positions in ascending order.
+  // When the threshold bin holds more than kTkCandMax keys (scores sharing
+  // their top 12 bits en masse) the general radix passes below take over.
+  if constexpr (kBitmap) {
+    if (L <= 2 * cache_keys && L <= kTkBitmapMaxLen &&
+        bitmap_path<kTkThreads>(a, L, row_scores, out_idx,
+        out_score, req, kv0, cache, hist_words, cand_pos, reinterpret_cast<uint32_t*>(sel_t),
+        wave_tot, sh_digit, sh_remaining, sh_count, sh_ncand)) {
+      return;
+    }
   }
 
   // The row is processed in blocks of cache_keys keys staged in LDS as

@@ -382,6 +382,54 @@ def test_mla_head_counts_below_128(heads):
     assert np.abs(l4.cpu().numpy() - r4l).max() <= 1e-3
 
 
+def test_topk_ties_in_the_threshold_bin_and_length_limits():
+    # rows whose k-th largest score is shared by several keys while the
+    # threshold's 12-bit bin stays small (the lowest tied positions are
+    # taken), rows whose tied keys are all taken, rows at 65536 keys and one
+    # past it, an odd length, and a row that starts at an odd float offset;
+    # selected scores are returned too.  The decision is on the same float32
+    # values: the selected sets and scores must equal the oracle's exactly.
+    rng = np.random.default_rng(77)
+    k = 2048
+    Lmax = 65537
+    specs = []
+    base = rng.standard_normal(40000).astype(np.float32)
+    order = np.argsort(-base, kind="stable")
+    r0 = base.copy()
+    r0[order[2000:2060]] = base[order[2030]]        # 60 ties straddle rank k: 48 taken
+    specs.append(r0)
+    r1 = base.copy()
+    r1[order[2040:2048]] = base[order[2047]]        # 8 ties, all taken
+    specs.append(r1)
+    r2 = base.copy()
+    r2[order[2048:2100]] = base[order[2047]]        # the k-th key and 52 equal ones below it
+    specs.append(r2)
+    specs.append(rng.standard_normal(65536).astype(np.float32) * 3.0 - 1.0)
+    specs.append(rng.standard_normal(65537).astype(np.float32))
+    specs.append(rng.standard_normal(40001).astype(np.float32))
+    r6 = -np.abs(rng.standard_normal(30000)).astype(np.float32)   # all negative, with -0.0 and +0.0
+    r6[:10] = -0.0
+    r6[10:20] = 0.0
+    specs.append(r6)
+    lens = np.array([x.size for x in specs], dtype=np.int32)
+    stride = Lmax + 2                                # rows start at 4-byte (not 16-byte) offsets
+    scores = np.full((len(specs), stride), np.nan, dtype=np.float32)
+    for i, r in enumerate(specs):
+        scores[i, : lens[i]] = r
+    dev_scores = torch.from_numpy(scores).to(gp.DEV)
+    kv_start = torch.zeros(len(specs), dtype=torch.int32, device=gp.DEV)
+    kv_len = torch.from_numpy(lens).to(gp.DEV)
+    idx, sc = ds.topk_select(dev_scores, kv_start, kv_len, Lmax, k, Lmax, want_score=True)
+    torch.cuda.synchronize()
+    got, got_sc = idx.cpu().numpy(), sc.cpu().numpy()
+    for i in range(len(specs)):
+        row = scores[i, : lens[i]]
+        want = np.sort(sa.topk_positions(row, k))
+        assert np.array_equal(got[i], want), f"row {i}: {np.setxor1d(got[i], want).size} differences"
+        want_sc = row[want] + np.float32(0.0)       # -0.0 is reported as +0.0
+        assert np.array_equal(got_sc[i], want_sc), f"row {i}: scores differ"
+
+
 def test_topk_rows_longer_than_the_cache():
     # rows longer than the 32768-key LDS cache: the threshold bucket is
     # compacted into the cache after the first radix pass when it fits, and
