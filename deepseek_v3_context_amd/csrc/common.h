@@ -163,12 +163,14 @@ ds_status launch_topk(const TopkArgs& a, hipStream_t s);
 constexpr int kMlaWidenedRowBytes = 576 * 2;
 ds_status launch_widen_fp8_rows(const void* codes, const float* scale, int32_t scale_shift,
                                 int64_t rows, void* out, hipStream_t s);
-// Rows longer than this are selected in two phases when there are few of
-// them (their candidates need topk_two_phase_bytes() of workspace).
+// Few rows longer than the single-workgroup bitmap selection takes (65536
+// keys) are selected in two phases, over segments of kTopkSegLen keys and
+// then over the segments' candidates (topk_two_phase_bytes() of workspace).
 constexpr int32_t kTopkSegLen = 8192;
 constexpr int32_t kTopkMax = 2048;
+constexpr int32_t kTopkOnePassMaxLen = 65536;
 inline bool topk_two_phase(int32_t n_q, int32_t max_kv_len) {
-  return max_kv_len > 2 * kTopkSegLen && n_q <= 256;
+  return max_kv_len > kTopkOnePassMaxLen && n_q <= 256;
 }
 inline size_t topk_two_phase_bytes(int32_t n_q, int32_t max_kv_len) {
   const int64_t n_seg = (static_cast<int64_t>(max_kv_len) + kTopkSegLen - 1) / kTopkSegLen;

@@ -38,7 +38,7 @@ constexpr int32_t kTkCacheKeys = 32768;   // 128 KiB of LDS
 // smaller LDS footprint, and with it two or three workgroups per CU.
 constexpr int kTkBins = 4096;
 constexpr int kTkCandMax = 2048;
-constexpr int32_t kTkBitmapMaxLen = 65536;
+constexpr int32_t kTkBitmapMaxLen = kTopkOnePassMaxLen;
 
 __device__ __forceinline__ int64_t topk_key_row(const TopkArgs& a, int32_t req,
                                                 int64_t l) {

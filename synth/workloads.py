@@ -123,6 +123,10 @@ _add(Workload("small_decode_paged_fp8", "decode", seed=14, n_req=6, len_lo=40,
               len_hi=5000, topk=256, page_size=64, kv_fmt="fp8",
               description="6 requests, lengths in [40, 5000], top-k 256; latent"
                           " KV and indexer keys e4m3fn, per-128-row scale"))
+_add(Workload("long_decode_paged", "decode", seed=15, n_req=3, len_lo=66000,
+              len_hi=80000, page_size=64,
+              description="3 requests with contexts past 65536 keys (the"
+                          " two-phase top-k); top-k 2048; bf16"))
 _add(replace(WORKLOADS["tiny_prefill_t256_cp4"], name="tiny_prefill_dense",
              seed=20, topk=256,
              description="tiny prefill with top-k >= context: dense causal"))

@@ -180,6 +180,12 @@ def test_decode_full_size_all_requests():
     _check_decode("decode_32req_paged", all_rows=True)
 
 
+def test_decode_contexts_past_65536_keys():
+    # rows longer than the one-pass selection takes: top-k in two phases
+    # (segments, then their candidates)
+    _check_decode("long_decode_paged", all_rows=True)
+
+
 # ------------------------------------------------------------------ edges
 
 def test_ranks_without_tokens_and_empty_requests():
