@@ -123,3 +123,29 @@ def test_full_size_sampled_rows(name):
     err, over, _ = _gate(got, _f64(a[rows].cpu()), _f64(w.cpu()))
     gp.say(f"  max|err|={err:.3e}")
     assert over <= 0, (name, err)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("N", [128, 256])
+def test_output_at_unaligned_address_and_stride(out_dtype, N):
+    # the output rows start one element past a 16-byte boundary and have an
+    # odd stride, so the row-piece stores of the epilogue cannot be 16-byte
+    # stores; M = 130 leaves a partial 64-row block.  Elements around the
+    # output window keep their canary value.
+    M, K = 130, 192
+    g = torch.Generator().manual_seed(21 + N)
+    a, w = _bf16((M, K), g, 1.0), _bf16((N, K), g, K ** -0.5)
+    ld = N + 3
+    buf = torch.full((M + 1, ld), 5.0, dtype=out_dtype, device=gp.DEV)
+    out = buf.view(-1)[1: 1 + M * ld].view(M, ld)[:, :N]
+    gp.say(f"[gpu] gemm output at an unaligned address: N={N} {out_dtype}")
+    ds.gemm_bf16_nt(a.to(gp.DEV), w.to(gp.DEV), out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64) if out_dtype == torch.float32 else _f64(out.cpu())
+    err, over, _ = _gate(got, _f64(a), _f64(w))
+    assert over <= 0, err
+    flat = buf.float().cpu().numpy().reshape(-1)
+    mask = np.ones(flat.size, bool)
+    for r in range(M):
+        mask[1 + r * ld: 1 + r * ld + N] = False
+    assert (flat[mask] == 5.0).all()
