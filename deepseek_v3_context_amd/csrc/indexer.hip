@@ -135,14 +135,13 @@ __device__ __forceinline__ float head_sum(const f32x16 (&acc)[kIxRowBlocks],
   return v;
 }
 
-// --------------------------------------------- prefill, pipelined path
-// A workgroup of 8 waves owns 8 consecutive queries (one per wave: A
-// fragments in 64 VGPRs, the 64 head weights of the query in 32 VGPRs) and
-// a chunk of absolute key rows.  Key tiles (128 bf16 or 256 fp8 rows) are
-// gathered straight into LDS with global_load_lds_dwordx4 (no VGPRs),
-// double-buffered so that the
-// gather of tile t+1 overlaps the MFMAs of tile t; every wave reads the
-// shared tile's B fragments from LDS.  Two waves per SIMD.
+// --------------------------------------------- prefill: key tiles in LDS
+// A workgroup of 8 waves works on 8 consecutive queries at a time (one per
+// wave: A fragments in 64 VGPRs, the 64 head weights of the query in 32
+// VGPRs).  Key tiles (128 bf16 or 256 fp8 rows) are gathered straight into
+// LDS with global_load_lds_dwordx4 (no VGPRs), double-buffered so that the
+// gather of the next tile overlaps the MFMAs of the current one; every wave
+// reads the shared tile's B fragments from LDS.  Two waves per SIMD.
 constexpr int kIxPWaves = 8;
 constexpr int kIxPHalf = 64;                       // keys per MFMA pass (two 32-key blocks)
 template <bool kFp8>
@@ -234,180 +233,6 @@ __device__ __forceinline__ bf16x8 ix_bfrag(const uint8_t* tile, int nb, int ks, 
   } else {
     return __builtin_bit_cast(bf16x8,
                               *reinterpret_cast<const uint4*>(row + ks * 32 + (lane >> 5) * 16));
-  }
-}
-
-// Key rows per workgroup: 21 bf16 tiles or 10 fp8 tiles, the most whose
-// scores still fit in LDS beside the two tile buffers.  Longer chunks mean
-// fewer workgroups per query block: on causal prefills of a few thousand
-// queries the grid then fits on the CUs in one round.
-template <bool kFp8>
-constexpr int32_t ix_chunk_keys() { return kFp8 ? 2560 : 2688; }
-
-template <bool kFp8>
-__global__ void __launch_bounds__(kWave * kIxPWaves)
-indexer_prefill_pipelined_kernel(IndexerArgs a, int32_t n_qblocks, int32_t n_chunks) {
-  constexpr int32_t chunk_keys = ix_chunk_keys<kFp8>();
-  static_assert(chunk_keys % IxTile<kFp8>::kTile == 0 && chunk_keys % kFp8BlockRows == 0,
-                "chunks hold whole tiles and whole fp8 scale blocks");
-  __shared__ int64_t q_lo[kIxPWaves], q_hi[kIxPWaves];
-  // scores of the chunk stay in LDS until the end: a global store inside
-  // the tile loop would make every wait for the next tile's gather
-  // (vmcnt counts stores too) also wait for the store to retire
-  __shared__ float sc[kIxPWaves][chunk_keys];
-  __shared__ float ksc[chunk_keys / kFp8BlockRows];   // fp8 key scales of the chunk
-  // Every workgroup reads the same key rows (the whole indexer key set of
-  // a prefill fits in each XCD's L2), so workgroups are left in the
-  // hardware's round-robin order over the XCDs, which spreads the causal
-  // work evenly; query blocks run in reverse so the longest rows start
-  // first.
-  const uint32_t id = blockIdx.x;
-  if (id >= static_cast<uint32_t>(n_qblocks) * n_chunks) return;
-  const int32_t qb = n_qblocks - 1 - static_cast<int32_t>(id / n_chunks);
-  const int32_t chunk = static_cast<int32_t>(id % n_chunks);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  if (tid < kIxPWaves) {
-    const int32_t j = qb * kIxPWaves + tid;
-    int64_t lo = 0, hi = 0;
-    if (j < a.n_q) {
-      lo = a.kv_start[j];
-      hi = lo + clamp_len(a, j);
-      if (lo < 0) lo = 0;
-      if (hi > a.k_rows) hi = a.k_rows;
-      if (hi < lo) hi = lo;
-    }
-    q_lo[tid] = lo;
-    q_hi[tid] = hi;
-  }
-  if constexpr (kFp8) {
-    if (tid < chunk_keys / kFp8BlockRows) {
-      const int64_t r0 = static_cast<int64_t>(chunk) * chunk_keys + tid * kFp8BlockRows;
-      ksc[tid] = r0 < a.k_rows ? a.k_scale[r0 / kFp8BlockRows] : 0.f;
-    }
-  }
-  __syncthreads();
-  int64_t rlo = INT64_MAX, rhi = 0;
-#pragma unroll
-  for (int i = 0; i < kIxPWaves; ++i) {
-    if (q_hi[i] > q_lo[i]) {
-      rlo = q_lo[i] < rlo ? q_lo[i] : rlo;
-      rhi = q_hi[i] > rhi ? q_hi[i] : rhi;
-    }
-  }
-  const int64_t c_lo = static_cast<int64_t>(chunk) * chunk_keys;
-  const int64_t c_hi = c_lo + chunk_keys;
-  rlo = rlo > c_lo ? rlo : c_lo;
-  rhi = rhi < c_hi ? rhi : c_hi;
-  if (rlo >= rhi) return;
-  const int64_t t_first = (rlo / kIxPHalf) * kIxPHalf;
-  constexpr int kTile = IxTile<kFp8>::kTile;
-  const int32_t n_tiles = static_cast<int32_t>(ceil_div(rhi - t_first, kTile));
-  const uint8_t* keys = static_cast<const uint8_t*>(a.k_idx);
-
-  // this wave's query: A fragments, head weights of the rows this lane's
-  // accumulator elements hold, causal range
-  const int32_t j = qb * kIxPWaves + wave;
-  const int64_t my_lo = q_lo[wave], my_hi = q_hi[wave];
-  const bool live = my_hi > my_lo;
-  bf16x8 qa[kIxRowBlocks][kIxKSteps];
-  float wv[kIxRowBlocks][16];
-  {
-    const uint16_t* q0 = static_cast<const uint16_t*>(a.q_idx) +
-                         static_cast<int64_t>(live ? j : 0) * kIxHeads * kIxDim;
-    const float* w0 = a.w + static_cast<int64_t>(live ? j : 0) * kIxHeads;
-#pragma unroll
-    for (int rb = 0; rb < kIxRowBlocks; ++rb) {
-#pragma unroll
-      for (int ks = 0; ks < kIxKSteps; ++ks) qa[rb][ks] = load_q_frag(q0, rb, ks, lane);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) wv[rb][i] = w0[rb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
-    }
-  }
-  float* srow = a.scores + static_cast<int64_t>(live ? j : 0) * a.score_stride;
-  IxSlots<kFp8> sl;
-  sl.init(wave, lane);
-  // query loads complete before any gather is in flight (a wait for them
-  // inside the tile loop would also wait for the gathers)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  ix_issue_tile<0, kFp8>(keys, a.k_rows, t_first, sl, wave);
-
-  auto step = [&](auto bufc, int t) {
-    constexpr int B = decltype(bufc)::value;
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gather of tile t landed
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();         // every wave's; tile t-1 fully consumed
-    asm volatile("" ::: "memory");
-    const int64_t base = t_first + static_cast<int64_t>(t) * kTile;
-    if (t + 1 < n_tiles) ix_issue_tile<1 - B, kFp8>(keys, a.k_rows, base + kTile, sl, wave);
-#pragma unroll
-    for (int hf = 0; hf < kTile / kIxPHalf; ++hf) {
-      const int64_t hbase = base + hf * kIxPHalf;
-      // (a tile can reach past the chunk when the block's range starts
-      // past the chunk's first 64 rows: those rows belong to the next chunk)
-      if (!live || hbase >= my_hi || hbase + kIxPHalf <= my_lo || hbase >= c_hi) continue;
-      const uint8_t* tile = ix_buf<B>() + hf * kIxPHalf * IxTile<kFp8>::kLdsRow;
-      // both 32-key column blocks at once: four independent accumulator
-      // chains per wave keep the MFMA pipe busy
-      f32x16 acc[2][kIxRowBlocks];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int rb = 0; rb < kIxRowBlocks; ++rb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[nb][rb][i] = 0.f;
-      bf16x8 b0 = ix_bfrag<kFp8>(tile, 0, 0, lane), b1 = ix_bfrag<kFp8>(tile, 1, 0, lane);
-#pragma unroll
-      for (int ks = 0; ks < kIxKSteps; ++ks) {
-        bf16x8 n0 = b0, n1 = b1;
-        if (ks + 1 < kIxKSteps) {
-          n0 = ix_bfrag<kFp8>(tile, 0, ks + 1, lane);
-          n1 = ix_bfrag<kFp8>(tile, 1, ks + 1, lane);
-        }
-#pragma unroll
-        for (int rb = 0; rb < kIxRowBlocks; ++rb) {
-          acc[0][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b0, acc[0][rb], 0, 0, 0);
-          acc[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b1, acc[1][rb], 0, 0, 0);
-        }
-        b0 = n0;
-        b1 = n1;
-        // bf16: one k-step per scheduling region, so that the compiler
-        // does not regroup the products into dependent chains across steps
-        // (the four products of a step go to four different accumulators).
-        // fp8 keeps the free schedule, which overlaps the conversions.
-        if constexpr (!kFp8) __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float v = 0.f;
-#pragma unroll
-        for (int rb = 0; rb < kIxRowBlocks; ++rb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], relu_raw(acc[nb][rb][i]), v);
-        // the other half of the heads sits in lanes l^32
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
-                                                         false, false);
-        v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const int64_t row = hbase + nb * 32 + (lane & 31);
-        if (lane < 32 && row >= my_lo && row < my_hi && row < c_hi) sc[wave][row - c_lo] = v;
-      }
-    }
-  };
-  for (int32_t t = 0; t < n_tiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_tiles) step(std::integral_constant<int, 1>{}, t + 1);
-  }
-  // write this wave's query's scores of the chunk (contiguous in the row)
-  if (live) {
-    const int64_t lo = my_lo > c_lo ? my_lo : c_lo;
-    const int64_t hi = my_hi < c_hi ? my_hi : c_hi;
-    for (int64_t r = lo + lane; r < hi; r += kWave) {
-      float v = sc[wave][r - c_lo];
-      if constexpr (kFp8) v *= ksc[(r - c_lo) / kFp8BlockRows];   // per-row fp8 scale
-      srow[r - my_lo] = v;
-    }
   }
 }
 
@@ -650,6 +475,444 @@ indexer_paged_mfma_kernel(IndexerArgs a) {
   }
 }
 
+// ------------------------------------------- prefill, balanced persistent path
+// The causal work of a prefill is very uneven over (query block, key range)
+// pairs: the late query blocks see every key, the early ones a few, and a
+// grid of one workgroup per pair leaves about half the workgroups with no
+// key at all (each still costs a dispatch and the reads of its ranges) and
+// the rest with 1 to 10 tiles.  Here one workgroup per CU takes an equal
+// share of the launch's work, in query-block order, and no workgroup is
+// empty.  Each step computes one key tile against the 8 queries of the
+// current block (8 waves, one query per wave, the tile gathered into LDS by
+// DMA, double-buffered).  The walk over tiles:
+//   - a query block's tiles are those of its causal key range [lo, hi) (the
+//     union of its 8 queries' ranges), cut into windows of kIxBWin keys,
+//     each window's tiles starting at its first 64-key half that has work;
+//   - the shares are equal in cost, not in tiles: a tile weighs kIxBTileW
+//     and entering a block (its query loads, whose latency nothing hides)
+//     weighs kIxBBlockW, so a share of many short blocks gets fewer tiles;
+//   - scores are staged in LDS per window and written out once the
+//     workgroup leaves the window (the next tile is in another window or
+//     query block, or its share ends): at the top of the next step, right
+//     after its gather, so that the stores complete under its products;
+//     fp8 key scales (one per 64-key half, loaded a tile ahead) are applied
+//     as the scores are staged;
+//   - the gather of the next tile is issued at the top of each step, also
+//     when that tile belongs to the next window or query block;
+//   - when the query block changes, each wave loads its new query's range
+//     during the last tile of the old block, and its A fragments and head
+//     weights right after that tile's products.
+// Set-up: every workgroup stages the launch's query ranges in LDS
+// (coalesced loads, all in flight), computes each query block's range and
+// tile count, scans the weights and tile counts, and takes the tiles that
+// start in its share
+// [W*b/G, W*(b+1)/G) of the total weight W.
+constexpr int32_t kIxBWin = 2048;    // keys per score window
+constexpr int kIxBMaxQb = 1024;      // query blocks per launch
+
+template <bool kFp8>
+__device__ __forceinline__ void ix_window(int32_t lo, int32_t len, int64_t w, int64_t& tfirst,
+                                          int32_t& ntiles) {
+  constexpr int kTile = IxTile<kFp8>::kTile;
+  const int64_t hi = static_cast<int64_t>(lo) + len;
+  const int64_t wlo = w * kIxBWin > lo ? w * kIxBWin : lo;
+  const int64_t whi = (w + 1) * kIxBWin < hi ? (w + 1) * kIxBWin : hi;
+  tfirst = (wlo / kIxPHalf) * kIxPHalf;
+  ntiles = static_cast<int32_t>(ceil_div(whi - tfirst, kTile));
+}
+
+// tiles of a block with union range [lo, lo + len): the sum of ix_window's
+// counts over the windows the range touches
+template <bool kFp8>
+__device__ __forceinline__ int64_t ix_block_tiles(int32_t lo, int32_t len) {
+  constexpr int kTile = IxTile<kFp8>::kTile;
+  if (len <= 0) return 0;
+  const int64_t hi = static_cast<int64_t>(lo) + len;
+  const int64_t w0 = lo / kIxBWin, w1 = (hi - 1) / kIxBWin;
+  const int64_t t0 = (lo / kIxPHalf) * kIxPHalf;
+  if (w0 == w1) return ceil_div(hi - t0, kTile);
+  return ceil_div((w0 + 1) * kIxBWin - t0, kTile) + (w1 - w0 - 1) * (kIxBWin / kTile) +
+         ceil_div(hi - w1 * kIxBWin, kTile);
+}
+
+// causal key range [lo, hi) of query j, clamped to the key rows (hi <= lo:
+// no work)
+__device__ __forceinline__ void ix_query_range(const IndexerArgs& a, int32_t j, int64_t& lo,
+                                               int64_t& hi) {
+  lo = 0;
+  hi = 0;
+  if (j < a.n_q) {
+    lo = a.kv_start[j];
+    hi = lo + clamp_len(a, j);
+    if (lo < 0) lo = 0;
+    if (hi > a.k_rows) hi = a.k_rows;
+    if (hi < lo) hi = lo;
+  }
+}
+
+template <bool kFp8>
+__global__ void __launch_bounds__(kWave * kIxPWaves)
+indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
+  using TL = IxTile<kFp8>;
+  constexpr int kTile = TL::kTile;
+  constexpr int kHalves = kTile / kIxPHalf;
+  // a 64-key half's products take about 3.3K clocks on the two waves of a
+  // SIMD; a block entry exposes one memory latency (about 7K clocks)
+  constexpr int64_t kIxBTileW = kFp8 ? 2 : 1;
+  constexpr int64_t kIxBBlockW = 1;
+  static_assert(kIxBWin % kTile == 0 && kIxBWin % kFp8BlockRows == 0,
+                "windows hold whole tiles and whole fp8 scale blocks");
+  static_assert(kIxPHalf <= kFp8BlockRows && kFp8BlockRows % kIxPHalf == 0,
+                "a 64-key half has one fp8 scale");
+  static_assert(2 * kWave * kIxPWaves >= kIxBMaxQb, "two query blocks per thread in the set-up");
+  __shared__ float sc[kIxPWaves][kIxBWin];                  // scores of the current window
+  __shared__ int32_t qb_lo[kIxBMaxQb], qb_len[kIxBMaxQb];   // union range of each block
+  __shared__ int64_t wave_tot[2][kIxPWaves];
+  __shared__ int64_t share_tiles[2];                        // tiles starting before g0, g1
+  __shared__ int32_t first_qb, first_off;
+  __shared__ int64_t first_lo[kIxPWaves], first_hi[kIxPWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- set-up: ranges, tiles and weights of blocks 2*tid and 2*tid + 1.
+  // The launch's query ranges are staged in LDS first (in the score
+  // buffer, free until the walk) with coalesced loads, all in flight.
+  int64_t ql[16], qh[16];
+  {
+    constexpr int kPer = kIxBMaxQb * kIxPWaves / (kWave * kIxPWaves);
+    static_assert(2 * kIxBMaxQb * kIxPWaves <= kIxPWaves * kIxBWin, "the ranges fit the score buffer");
+    int32_t* s_start = reinterpret_cast<int32_t*>(&sc[0][0]);
+    int32_t* s_len = s_start + kIxBMaxQb * kIxPWaves;
+    const int32_t j0 = qb0 * kIxPWaves;
+    const int32_t nj = a.n_q - j0 < n_qb * kIxPWaves ? a.n_q - j0 : n_qb * kIxPWaves;
+    int32_t vs[kPer], vl[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int32_t i = u * kWave * kIxPWaves + tid;
+      const int32_t ic = i < nj ? i : nj - 1;
+      vs[u] = a.kv_start[j0 + ic];
+      vl[u] = a.kv_len[j0 + ic];
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int32_t i = u * kWave * kIxPWaves + tid;
+      if (i < nj) {
+        s_start[i] = vs[u];
+        s_len[i] = vl[u];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int32_t q = 2 * tid + i / 8;
+      const int32_t jl = q * kIxPWaves + i % 8;
+      const bool in = q < n_qb && jl < nj;
+      const int32_t st = in ? s_start[jl] : 0, ln = in ? s_len[jl] : 0;
+      const int64_t lo = st < 0 ? 0 : st;
+      int64_t hi = static_cast<int64_t>(st) + (ln < 0 ? 0 : (ln > a.max_kv_len ? a.max_kv_len : ln));
+      hi = hi > a.k_rows ? a.k_rows : hi;
+      const bool ok = in && hi > lo;
+      ql[i] = ok ? lo : 0;
+      qh[i] = ok ? hi : 0;
+    }
+  }
+  int64_t nt[2], wt[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    int64_t lo = INT64_MAX, hi = 0;
+#pragma unroll
+    for (int i = 8 * k; i < 8 * k + 8; ++i) {
+      if (qh[i] > ql[i]) {
+        lo = ql[i] < lo ? ql[i] : lo;
+        hi = qh[i] > hi ? qh[i] : hi;
+      }
+    }
+    const int32_t len = hi > lo ? static_cast<int32_t>(hi - lo) : 0;
+    const int32_t l32 = hi > lo ? static_cast<int32_t>(lo) : 0;
+    nt[k] = ix_block_tiles<kFp8>(l32, len);
+    wt[k] = nt[k] > 0 ? kIxBTileW * nt[k] + kIxBBlockW : 0;
+    const int32_t q = 2 * tid + k;
+    if (q < n_qb) {
+      qb_lo[q] = l32;
+      qb_len[q] = len;
+    }
+  }
+  const int64_t incl_w = wave_incl_scan(wt[0] + wt[1], lane);
+  const int64_t incl_t = wave_incl_scan(nt[0] + nt[1], lane);
+  if (lane == kWave - 1) {
+    wave_tot[0][wave] = incl_w;
+    wave_tot[1][wave] = incl_t;
+  }
+  __syncthreads();
+  int64_t bw = 0, bt = 0, sw = 0, stt = 0;
+#pragma unroll
+  for (int w = 0; w < kIxPWaves; ++w) {
+    const int64_t x = wave_tot[0][w], y = wave_tot[1][w];
+    bw += w < wave ? x : 0;
+    bt += w < wave ? y : 0;
+    sw += x;
+    stt += y;
+  }
+  const int64_t w_total = lane_value(sw, 0), t_total = lane_value(stt, 0);
+  if (w_total == 0) return;
+  // weight and tile prefixes of this thread's blocks
+  int64_t pw[2], pt[2];
+  pw[0] = bw + incl_w - wt[0] - wt[1];
+  pw[1] = pw[0] + wt[0];
+  pt[0] = bt + incl_t - nt[0] - nt[1];
+  pt[1] = pt[0] + nt[0];
+  const int64_t g0 = w_total * blockIdx.x / gridDim.x;
+  const int64_t g1 = w_total * (blockIdx.x + 1) / gridDim.x;
+  // tile i of a block starts at weight pw + kIxBBlockW + i * kIxBTileW and
+  // belongs to the share its start falls in: count the tiles starting
+  // before g0 and before g1
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    auto before = [&](int64_t g) {
+      int64_t c = g - pw[k] - kIxBBlockW;
+      c = c <= 0 ? 0 : ceil_div(c, kIxBTileW);
+      return pt[k] + (c < nt[k] ? c : nt[k]);
+    };
+    if (wt[k] > 0 && pw[k] <= g0 && g0 < pw[k] + wt[k]) share_tiles[0] = before(g0);
+    if (wt[k] > 0 && pw[k] <= g1 && g1 < pw[k] + wt[k]) share_tiles[1] = before(g1);
+  }
+  if (tid == 0 && g1 >= w_total) share_tiles[1] = t_total;
+  __syncthreads();
+  const int64_t f0 = lane_value(share_tiles[0], 0), f1 = lane_value(share_tiles[1], 0);
+  if (f1 <= f0) return;   // the whole workgroup: no barrier below is skipped by part of it
+  // the block holding tile f0 (the share's first), and its queries' ranges
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (nt[k] > 0 && pt[k] <= f0 && f0 < pt[k] + nt[k]) {
+      first_qb = 2 * tid + k;
+      first_off = static_cast<int32_t>(f0 - pt[k]);
+#pragma unroll
+      for (int i = 0; i < kIxPWaves; ++i) {
+        first_lo[i] = ql[8 * k + i];
+        first_hi[i] = qh[8 * k + i];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- walk state (wave-uniform): block qb, window w, tile t of the
+  // window's n_t tiles starting at row tf
+  struct Pos {
+    int32_t qb, t, n_t;
+    int64_t w, tf;
+  };
+  auto block_lo = [&](int32_t q) { return __builtin_amdgcn_readfirstlane(qb_lo[q]); };
+  auto block_len = [&](int32_t q) { return __builtin_amdgcn_readfirstlane(qb_len[q]); };
+  auto enter_window = [&](Pos& p) { ix_window<kFp8>(block_lo(p.qb), block_len(p.qb), p.w, p.tf, p.n_t); };
+  auto advance = [&](Pos p) {
+    if (p.t + 1 < p.n_t) {
+      ++p.t;
+      return p;
+    }
+    p.t = 0;
+    const int32_t lo = block_lo(p.qb), len = block_len(p.qb);
+    if ((p.w + 1) * kIxBWin < static_cast<int64_t>(lo) + len) {
+      ++p.w;
+    } else {
+      // next block with work (there is one: the share has tiles left)
+      do {
+        ++p.qb;
+      } while (block_len(p.qb) == 0);
+      p.w = block_lo(p.qb) / kIxBWin;
+    }
+    enter_window(p);
+    return p;
+  };
+  Pos cur;
+  cur.qb = __builtin_amdgcn_readfirstlane(first_qb);
+  cur.w = block_lo(cur.qb) / kIxBWin;
+  cur.t = 0;
+  enter_window(cur);
+  {
+    int32_t off = __builtin_amdgcn_readfirstlane(first_off);
+    while (off >= cur.n_t) {
+      off -= cur.n_t;
+      ++cur.w;
+      enter_window(cur);
+    }
+    cur.t = off;
+  }
+
+  // this wave's query in the current block: range, A fragments, weights
+  auto query_of = [&](int32_t q) { return (qb0 + q) * kIxPWaves + wave; };
+  int64_t my_lo = lane_value(first_lo[wave], 0), my_hi = lane_value(first_hi[wave], 0);
+  bf16x8 qa[kIxRowBlocks][kIxKSteps];
+  float wv[kIxRowBlocks][16];
+  auto load_query = [&](int32_t j, bool live) {
+    const uint16_t* q0 = static_cast<const uint16_t*>(a.q_idx) +
+                         static_cast<int64_t>(live ? j : 0) * kIxHeads * kIxDim;
+    const float* w0 = a.w + static_cast<int64_t>(live ? j : 0) * kIxHeads;
+#pragma unroll
+    for (int rb = 0; rb < kIxRowBlocks; ++rb) {
+#pragma unroll
+      for (int ks = 0; ks < kIxKSteps; ++ks) qa[rb][ks] = load_q_frag(q0, rb, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wv[rb][i] = w0[rb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
+    }
+  };
+  // fp8 key scales of a tile's 64-key halves, loaded one tile ahead (the
+  // top-of-step wait covers them); a tile's buffer parity picks the set
+  float ksc[2][kHalves];
+  auto load_scales = [&](float (&dst)[kHalves], int64_t base) {
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) {
+        int64_t r = base + hf * kIxPHalf;
+        r = r < a.k_rows ? r : a.k_rows - 1;
+        dst[hf] = a.k_scale[r / kFp8BlockRows];
+      }
+    }
+  };
+  const uint8_t* keys = static_cast<const uint8_t*>(a.k_idx);
+  IxSlots<kFp8> sl;
+  sl.init(wave, lane);
+  // the first tile's gather goes out with the query loads (the first
+  // step's wait covers both)
+  load_query(query_of(cur.qb), my_hi > my_lo);
+  load_scales(ksc[0], cur.tf + static_cast<int64_t>(cur.t) * kTile);
+  ix_issue_tile<0, kFp8>(keys, a.k_rows, cur.tf + static_cast<int64_t>(cur.t) * kTile, sl, wave);
+
+  int64_t left = f1 - f0;        // tiles of the share not yet computed
+  int32_t seg_t0 = cur.t;        // first tile of the current window computed here
+  // This wave's scores of rows [lo, hi) of the window starting at row c_lo
+  // go to its query's score row (position = row - q_lo), all LDS reads of a
+  // group of four rows per lane ahead of its stores.
+  auto flush = [&](int64_t lo, int64_t hi, int64_t c_lo, float* srow, int64_t q_lo) {
+    for (int64_t r0 = lo; r0 < hi; r0 += 4 * kWave) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t r = r0 + u * kWave + lane;
+        v[u] = r < hi ? sc[wave][r - c_lo] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t r = r0 + u * kWave + lane;
+        if (r < hi) srow[r - q_lo] = v[u];
+      }
+    }
+  };
+  // A window's flush waits for the next step (when the workgroup has one):
+  // issued there right after the next gather, the stores then complete
+  // under that step's products instead of delaying its top-of-step wait.
+  int64_t fl_lo = 0, fl_hi = 0, fl_clo = 0, fl_qlo = 0;
+  float* fl_row = a.scores;
+  auto step = [&](auto bufc) {
+    constexpr int B = decltype(bufc)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's gather of this tile landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();         // every wave's; the other buffer fully consumed
+    asm volatile("" ::: "memory");
+    const bool more = left > 1;
+    Pos nxt = cur;
+    if (more) {
+      nxt = advance(cur);
+      const int64_t nbase = nxt.tf + static_cast<int64_t>(nxt.t) * kTile;
+      ix_issue_tile<1 - B, kFp8>(keys, a.k_rows, nbase, sl, wave);
+      load_scales(ksc[1 - B], nbase);
+    }
+    if (fl_hi > fl_lo) {   // the previous window's rows (read before this step's score writes)
+      flush(fl_lo, fl_hi, fl_clo, fl_row, fl_qlo);
+      fl_hi = fl_lo;
+    }
+    const bool new_block = more && nxt.qb != cur.qb;
+    int64_t nx_lo = my_lo, nx_hi = my_hi;
+    if (new_block) ix_query_range(a, query_of(nxt.qb), nx_lo, nx_hi);
+
+    const bool live = my_hi > my_lo;
+    const int64_t c_lo = cur.w * kIxBWin, c_hi = c_lo + kIxBWin;
+    const int64_t base = cur.tf + static_cast<int64_t>(cur.t) * kTile;
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) {
+      const int64_t hbase = base + hf * kIxPHalf;
+      // (a window's last tile can reach past the window: those rows are
+      // the next window's)
+      if (!live || hbase >= my_hi || hbase + kIxPHalf <= my_lo || hbase >= c_hi) continue;
+      const uint8_t* tile = ix_buf<B>() + hf * kIxPHalf * TL::kLdsRow;
+      f32x16 acc[2][kIxRowBlocks];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int rb = 0; rb < kIxRowBlocks; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][rb][i] = 0.f;
+      bf16x8 b0 = ix_bfrag<kFp8>(tile, 0, 0, lane), b1 = ix_bfrag<kFp8>(tile, 1, 0, lane);
+#pragma unroll
+      for (int ks = 0; ks < kIxKSteps; ++ks) {
+        bf16x8 n0 = b0, n1 = b1;
+        if (ks + 1 < kIxKSteps) {
+          n0 = ix_bfrag<kFp8>(tile, 0, ks + 1, lane);
+          n1 = ix_bfrag<kFp8>(tile, 1, ks + 1, lane);
+        }
+#pragma unroll
+        for (int rb = 0; rb < kIxRowBlocks; ++rb) {
+          acc[0][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b0, acc[0][rb], 0, 0, 0);
+          acc[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], b1, acc[1][rb], 0, 0, 0);
+        }
+        b0 = n0;
+        b1 = n1;
+        if constexpr (!kFp8) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float v = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < kIxRowBlocks; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v = fmaf(wv[rb][i], relu_raw(acc[nb][rb][i]), v);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                         false, false);
+        v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        if constexpr (kFp8) v *= ksc[B][hf];   // the key rows' fp8 scale
+        const int64_t row = hbase + nb * 32 + (lane & 31);
+        if (lane < 32 && row >= my_lo && row < my_hi && row < c_hi) sc[wave][row - c_lo] = v;
+      }
+    }
+    // leaving the window: this wave's scores of the rows computed here
+    // (tiles seg_t0..t of the window) go out, at the next step's top or,
+    // at the end of the share, now
+    if (!more || nxt.qb != cur.qb || nxt.w != cur.w) {
+      if (live) {
+        int64_t lo = cur.tf + static_cast<int64_t>(seg_t0) * kTile;
+        int64_t hi = base + kTile;
+        lo = lo > my_lo ? lo : my_lo;
+        hi = hi < my_hi ? hi : my_hi;
+        hi = hi < c_hi ? hi : c_hi;
+        float* srow = a.scores + static_cast<int64_t>(query_of(cur.qb)) * a.score_stride;
+        if (more) {
+          fl_lo = lo;
+          fl_hi = hi;
+          fl_clo = c_lo;
+          fl_row = srow;
+          fl_qlo = my_lo;
+        } else {
+          flush(lo, hi, c_lo, srow, my_lo);
+        }
+      }
+      seg_t0 = nxt.t;
+    }
+    if (new_block) {
+      my_lo = nx_lo;
+      my_hi = nx_hi;
+      load_query(query_of(nxt.qb), my_hi > my_lo);
+    }
+    cur = nxt;
+    --left;
+  };
+  while (true) {
+    step(std::integral_constant<int, 0>{});
+    if (left == 0) break;
+    step(std::integral_constant<int, 1>{});
+    if (left == 0) break;
+  }
+}
+
 // ------------------------------------------------------------------ host
 
 
@@ -672,17 +935,20 @@ ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
     else indexer_paged_mfma_kernel<false><<<blocks, kWave * kIxWaves, 0, s>>>(a);
     return check_launch("indexer_scores (paged)");
   }
+  // one workgroup per CU, each an equal share of the key tiles of up to
+  // kIxBMaxQb query blocks per launch
   const int32_t n_qblocks = static_cast<int32_t>(ceil_div(a.n_q, kIxPWaves));
-  const int32_t n_chunks =
-      static_cast<int32_t>(ceil_div(a.k_rows, fp8 ? ix_chunk_keys<true>() : ix_chunk_keys<false>()));
-  const uint32_t grid = static_cast<uint32_t>(round_up(static_cast<int64_t>(n_qblocks) * n_chunks, 8));
-  if (fp8)
-    indexer_prefill_pipelined_kernel<true><<<grid, kWave * kIxPWaves, 0, s>>>(
-        a, n_qblocks, n_chunks);
-  else
-    indexer_prefill_pipelined_kernel<false><<<grid, kWave * kIxPWaves, 0, s>>>(
-        a, n_qblocks, n_chunks);
-  return check_launch("indexer_scores (prefill)");
+  const unsigned grid = static_cast<unsigned>(device_cu_count());
+  for (int32_t qb0 = 0; qb0 < n_qblocks; qb0 += kIxBMaxQb) {
+    const int32_t n = n_qblocks - qb0 < kIxBMaxQb ? n_qblocks - qb0 : kIxBMaxQb;
+    if (fp8)
+      indexer_prefill_balanced_kernel<true><<<grid, kWave * kIxPWaves, 0, s>>>(a, qb0, n);
+    else
+      indexer_prefill_balanced_kernel<false><<<grid, kWave * kIxPWaves, 0, s>>>(a, qb0, n);
+    const ds_status st = check_launch("indexer_scores (prefill)");
+    if (st != DS_OK) return st;
+  }
+  return DS_OK;
 }
 
 }  // namespace ds32cp

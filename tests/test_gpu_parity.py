@@ -136,6 +136,13 @@ def _check_prefill(name, all_rows):
     assert np.array_equal(g["kv_bytes"].reshape(T, -1), kv_bytes)
     ki_bytes = np.ascontiguousarray(inp["k_idx"]).view(np.uint8).reshape(T, -1)
     assert np.array_equal(g["ki_bytes"].reshape(T, -1), ki_bytes)
+    # S3 on every row (a property that holds at any size): each query's
+    # scores over its whole causal range were written, and nothing past it
+    sc = g["scores"]
+    written = np.arange(sc.shape[1])[None, :] < g["kv_len"].astype(np.int64)[:, None]
+    assert np.isfinite(sc[written]).all(), "a causal score was not written"
+    assert np.isnan(sc[~written]).all(), "a score past kv_len was written"
+    del written
     rows = list(range(n)) if all_rows else _sample_rows(n, wl.seed, om["local_cu"])
     if not all_rows:   # every request's first and last local row is among them
         for lo, hi in zip(om["local_cu"][:-1], om["local_cu"][1:]):
@@ -285,6 +292,49 @@ def test_decode_page_boundaries():
     gi = idx.cpu().numpy()
     for j, s in enumerate(sel):
         assert set(gi[j][gi[j] >= 0].tolist()) == set(s["topk_idx"][s["topk_idx"] >= 0].tolist())
+
+
+@pytest.mark.parametrize("kfmt", ["bf16", "fp8"])
+def test_prefill_indexer_arbitrary_ranges_and_two_launches(kfmt):
+    # The contiguous (prefill) indexer on ranges no causal prefill has:
+    # empty ranges, starts inside a 64-key half and on either side of a
+    # 2048-key score window, ranges ending at the last key row, and 8200
+    # queries, so that the query blocks (8 queries each) take two launches.
+    # Every row: scores written over exactly its range.  Sampled rows (the
+    # blocks around the launch boundary and every planted case) against the
+    # oracle.
+    rng = np.random.default_rng(31 if kfmt == "bf16" else 32)
+    K, n, max_len = 5000, 8200, 3000
+    kv_start = rng.integers(0, K, n).astype(np.int32)
+    kv_len = np.minimum(rng.integers(0, max_len + 1, n), K - kv_start).astype(np.int32)
+    planted = {0: (0, 0), 5: (0, 1), 6: (63, 2), 7: (2047, 2), 8: (2048, 700), 9: (2040, 2100),
+               100: (4999, 1), 101: (K - 3000, 3000), 8183: (1, 0), 8184: (4095, 905),
+               8191: (0, 3000), 8192: (130, 2), 8199: (4000, 1000)}
+    for j, (st, ln) in planted.items():
+        kv_start[j], kv_len[j] = st, ln
+    kv_len[1000:1040] = 0                        # five query blocks with no work at all
+    from synth.draw import to_bf16_bits, to_e4m3fn_blocks
+    ki = (rng.standard_normal((K, 128)) / np.sqrt(128)).astype(np.float32)
+    ki_v, ki_scale = (to_bf16_bits(ki), None) if kfmt == "bf16" else to_e4m3fn_blocks(ki)
+    qi_b = to_bf16_bits((rng.standard_normal((n, 64, 128)) / np.sqrt(128)).astype(np.float32))
+    w = (rng.standard_normal((n, 64)) / 8).astype(np.float32)
+    ks_dev = None if ki_scale is None else torch.from_numpy(ki_scale).to(gp.DEV)
+    gp.say(f"[gpu] prefill indexer, arbitrary ranges, {n} queries, {kfmt} keys")
+    sc = ds.indexer_scores(gp.to_dev(qi_b, "bf16"), torch.from_numpy(w).to(gp.DEV),
+                           gp.to_dev(ki_v, kfmt), torch.from_numpy(kv_start).to(gp.DEV),
+                           torch.from_numpy(kv_len).to(gp.DEV), max_len, k_scale=ks_dev)
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    written = np.arange(max_len)[None, :] < kv_len.astype(np.int64)[:, None]
+    assert np.isfinite(sc[written]).all(), "a score in range was not written"
+    assert np.isnan(sc[~written]).all(), "a score past the range was written"
+    rows = sorted(set(planted) | set(range(8176, 8200)) | set(range(1000, 1041, 8)) |
+                  set(rng.choice(n, 24, replace=False).tolist()))
+    meta = {"kv_start": kv_start, "kv_len": kv_len}
+    sel = opl.indexer_topk_rows(rows, meta, qi_b, "bf16", w, ki_v, kfmt, ki_scale, 16)
+    for j, s in zip(rows, sel):
+        L = int(kv_len[j])
+        assert np.all(np.abs(sc[j, :L] - s["scores64"]) <= SCORE_ATOL), f"row {j}: score error"
 
 
 @pytest.mark.parametrize("kfmt", ["bf16", "fp8"])
