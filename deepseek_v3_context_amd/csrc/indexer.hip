@@ -842,6 +842,11 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
         for (int rb = 0; rb < kIxRowBlocks; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[nb][rb][i] = 0.f;
+      // The two waves of a SIMD leave each barrier together and would run
+      // their products and their head sums in step; a raised priority for
+      // the products lets a wave in its head sum yield the issue slots to
+      // the other's MFMAs, so the vector work fills the matrix core's gaps.
+      __builtin_amdgcn_s_setprio(1);
       bf16x8 b0 = ix_bfrag<kFp8>(tile, 0, 0, lane), b1 = ix_bfrag<kFp8>(tile, 1, 0, lane);
 #pragma unroll
       for (int ks = 0; ks < kIxKSteps; ++ks) {
@@ -859,6 +864,7 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
         b1 = n1;
         if constexpr (!kFp8) __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         float v = 0.f;
