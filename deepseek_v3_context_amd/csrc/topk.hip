@@ -31,6 +31,7 @@ namespace ds32cp {
 
 constexpr int kTkPer = 8;                 // consecutive keys per thread and step
 constexpr int32_t kTkCacheKeys = 32768;   // 128 KiB of LDS
+constexpr int32_t kTkSmallCacheKeys = 4096;   // 16 KiB: three workgroups per CU (kMode 3)
 // Bitmap path: bins of the first digit (the top 12 bits of the 32-bit
 // key), the most threshold-bucket keys it resolves in LDS, and the longest
 // row it takes (16-bit keys in the cache; positions fit in 16 bits).  Only
@@ -81,7 +82,7 @@ __device__ __forceinline__ uint32_t tk_block_scan(uint32_t v, int lane, int wave
 // Bitmap path of the single-workgroup selection (see topk_kernel).  Returns
 // false, having written nothing, when the threshold bin holds more than
 // kTkCandMax keys.  Uniform control flow: every thread takes every branch.
-template <int kTkThreads>
+template <int kTkThreads, bool kCached>
 __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_scores,
                             int32_t* out_idx, float* out_score, int32_t req, int64_t kv0,
                             uint32_t* cache, uint32_t* hw, uint16_t* cand_pos,
@@ -124,7 +125,7 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
   const bool vec = (reinterpret_cast<uintptr_t>(row_scores) & 15u) == 0;
   // 16 loads of 16 bytes in flight per thread: a row of 65536 keys in one
   // round (this pass waits on memory, not on its arithmetic)
-  constexpr int kU = 16;
+  constexpr int kU = kCached ? 16 : 8;
   for (int32_t r0 = 0; r0 < L; r0 += 4 * kTkThreads * kU) {
     float4 v[kU];
 #pragma unroll
@@ -147,13 +148,15 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
       uint32_t key[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) key[e] = float_order_key(f[e]);
-      if (t + 4 <= L) {
-        *reinterpret_cast<uint2*>(c16 + t) =
-            make_uint2((key[0] >> 16) | (key[1] & 0xffff0000u), (key[2] >> 16) | (key[3] & 0xffff0000u));
-      } else {
+      if constexpr (kCached) {
+        if (t + 4 <= L) {
+          *reinterpret_cast<uint2*>(c16 + t) =
+              make_uint2((key[0] >> 16) | (key[1] & 0xffff0000u), (key[2] >> 16) | (key[3] & 0xffff0000u));
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (t + e < L) c16[t + e] = static_cast<uint16_t>(key[e] >> 16);
+          for (int e = 0; e < 4; ++e)
+            if (t + e < L) c16[t + e] = static_cast<uint16_t>(key[e] >> 16);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -179,7 +182,33 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
     uint32_t bits = 0, tbits = 0;
     if (w < n_words) {
       const int32_t p0 = w << 5;
-      if (p0 + 32 <= L) {
+      if constexpr (!kCached) {
+        // the row again from memory (L2 or HBM): 32 keys per word
+        float4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int32_t t = p0 + 4 * q;
+          if (vec && t + 4 <= L) {
+            v[q] = *reinterpret_cast<const float4*>(row_scores + t);
+          } else {
+            v[q].x = t < L ? row_scores[t] : 0.f;
+            v[q].y = t + 1 < L ? row_scores[t + 1] : 0.f;
+            v[q].z = t + 2 < L ? row_scores[t + 2] : 0.f;
+            v[q].w = t + 3 < L ? row_scores[t + 3] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float f[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int32_t t = p0 + 4 * q + e;
+            const uint32_t b = float_order_key(f[e]) >> 20;
+            bits |= (t < L && b > T ? 1u : 0u) << (4 * q + e);
+            tbits |= (t < L && b == T ? 1u : 0u) << (4 * q + e);
+          }
+        }
+      } else if (p0 + 32 <= L) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint4 x = *reinterpret_cast<const uint4*>(c16 + p0 + 8 * q);
@@ -318,11 +347,19 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
 //   n_seg*k candidates, which are in position order; padding scores are
 //   -inf, below every finite score (a key scored -inf is an unmapped one,
 //   whose row is -1 like a padding entry's, so ties there change nothing).
+// kMode 3: kMode 0 for launches of many long rows (512 threads, three
+//   workgroups per CU): the bitmap path reads the row twice from memory
+//   instead of caching it in LDS, and the general path works on a small
+//   block cache.
 template <int kTkThreads, int kMode>
-__global__ void __launch_bounds__(kTkThreads)
-topk_kernel(TopkArgs a, int32_t cache_keys) {
+__device__ __forceinline__ void topk_body(const TopkArgs& a, int32_t cache_keys) {
   constexpr int kTkWaves = kTkThreads / kWave;
-  constexpr bool kBitmap = kMode == 0 && kTkThreads == 1024;
+  // the bitmap path: with the row's top 16 bits cached in LDS (kMode 0,
+  // 1024 threads), or reading the row twice from memory (kMode 3: 512
+  // threads and a small LDS footprint, so that three workgroups share a CU
+  // and one's memory passes run under the others' LDS and ALU work)
+  constexpr bool kBitmap = (kMode == 0 && kTkThreads == 1024) || kMode == 3;
+  static_assert(kMode != 3 || kTkThreads == 512, "kMode 3 is the 512-thread kernel");
   extern __shared__ __align__(16) uint32_t cache[];
   // one 256-bin histogram per wave (less contention); the bitmap path uses
   // the same words as one 4096-bin histogram, then as its bitmaps
@@ -412,8 +449,8 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   // When the threshold bin holds more than kTkCandMax keys (scores sharing
   // their top 12 bits en masse) the general radix passes below take over.
   if constexpr (kBitmap) {
-    if (L <= 2 * cache_keys && L <= kTkBitmapMaxLen &&
-        bitmap_path<kTkThreads>(a, L, row_scores, out_idx,
+    if ((kMode == 3 || L <= 2 * cache_keys) && L <= kTkBitmapMaxLen &&
+        bitmap_path<kTkThreads, kMode == 0>(a, L, row_scores, out_idx,
         out_score, req, kv0, cache, hist_words, cand_pos, reinterpret_cast<uint32_t*>(sel_t),
         wave_tot, sh_digit, sh_remaining, sh_count, sh_ncand)) {
       return;
@@ -537,7 +574,7 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
     mask |= 255u << shift;
     remaining = sh_remaining;
     __syncthreads();
-    if (kMode == 0 && shift == 24 && !cached && sh_count <= static_cast<uint32_t>(cache_keys)) {
+    if ((kMode == 0 || kMode == 3) && shift == 24 && !cached && sh_count <= static_cast<uint32_t>(cache_keys)) {
       // uniform: every thread read the same sh_count
       if (tid == 0) sh_ncand = 0;
       __syncthreads();   // (the cache's last staged block is fully counted)
@@ -635,6 +672,17 @@ topk_kernel(TopkArgs a, int32_t cache_keys) {
   }
 }
 
+template <int kTkThreads, int kMode>
+__global__ void __launch_bounds__(kTkThreads) topk_kernel(TopkArgs a, int32_t cache_keys) {
+  topk_body<kTkThreads, kMode>(a, cache_keys);
+}
+
+// kMode 3: three workgroups of 512 threads per CU, so at most 80 VGPRs
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6)))
+topk_rows_kernel(TopkArgs a, int32_t cache_keys) {
+  topk_body<512, 3>(a, cache_keys);
+}
+
 template <int kThreads, int kMode>
 static void topk_set_smem() {
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<kThreads, kMode>),
@@ -669,9 +717,18 @@ ds_status launch_topk(const TopkArgs& a, hipStream_t s) {
   }
   const int32_t cache_keys = a.max_kv_len < kTkCacheKeys ? a.max_kv_len : kTkCacheKeys;
   const size_t smem = sizeof(uint32_t) * static_cast<size_t>(cache_keys > 0 ? cache_keys : 1);
-  // long rows: more waves per row to keep more keys in flight
-  if (a.max_kv_len > 16384) topk_kernel<1024, 0><<<a.n_q, 1024, smem, s>>>(a, cache_keys);
-  else topk_kernel<512, 0><<<a.n_q, 512, smem, s>>>(a, cache_keys);
+  if (a.max_kv_len > 16384 && a.max_kv_len <= kTkBitmapMaxLen && a.n_q >= 2 * device_cu_count()) {
+    // many long rows: three rows per CU, the memory passes of one under the
+    // LDS and ALU work of the others; a small block cache for the rare rows
+    // that leave the bitmap path
+    const int32_t ck = a.max_kv_len < kTkSmallCacheKeys ? a.max_kv_len : kTkSmallCacheKeys;
+    topk_rows_kernel<<<a.n_q, 512, sizeof(uint32_t) * ck, s>>>(a, ck);
+  } else if (a.max_kv_len > 16384) {
+    // few long rows: more waves per row to keep more keys in flight
+    topk_kernel<1024, 0><<<a.n_q, 1024, smem, s>>>(a, cache_keys);
+  } else {
+    topk_kernel<512, 0><<<a.n_q, 512, smem, s>>>(a, cache_keys);
+  }
   return check_launch("topk_select");
 }
 

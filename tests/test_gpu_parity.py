@@ -486,6 +486,64 @@ def test_topk_ties_in_the_threshold_bin_and_length_limits():
         assert np.array_equal(got_sc[i], want_sc), f"row {i}: scores differ"
 
 
+def test_topk_many_long_rows_three_workgroups_per_cu():
+    # A launch of more than 512 rows longer than 16384 keys takes the
+    # 512-thread selection that runs three rows per CU and reads each row
+    # twice from memory instead of caching it in LDS (its general path
+    # stages blocks of 4096 keys).  The planted rows of the two tests around
+    # this one, at a stride that starts every row at a 4-byte offset, among
+    # random rows of 2049 to 65536 keys; sets and returned scores must equal
+    # the oracle's exactly.
+    rng = np.random.default_rng(91)
+    k, Lmax, n = 2048, 65536, 530
+    base = rng.standard_normal(40000).astype(np.float32)
+    order = np.argsort(-base, kind="stable")
+    specs = []
+    for lo, hi, src in ((2000, 2060, 2030), (2040, 2048, 2047), (2048, 2100, 2047)):
+        r = base.copy()
+        r[order[lo:hi]] = base[order[src]]
+        specs.append(r)
+    specs.append(rng.standard_normal(65536).astype(np.float32) * 3.0 - 1.0)
+    specs.append(rng.standard_normal(40001).astype(np.float32))
+    r = -np.abs(rng.standard_normal(30000)).astype(np.float32)
+    r[:10], r[10:20] = -0.0, 0.0
+    specs.append(r)
+    specs.append(np.full(40000, 0.5, dtype=np.float32))                       # all tied
+    specs.append(rng.choice(np.array([-1.0, 0.25, 0.5, 2.0], dtype=np.float32), 40000))
+    r = (1.0 + rng.random(36000)).astype(np.float32)
+    r[rng.choice(36000, 2000, replace=False)] = 4.0
+    specs.append(r)
+    r = rng.standard_normal(40000).astype(np.float32)
+    r[(np.arange(2048) * 40000 + 20000) // 2048] = -5.0
+    specs.append(r)
+    specs.append(np.concatenate([rng.standard_normal(30000).astype(np.float32) * 1e-3 + 7.0,
+                                 np.zeros(10000, np.float32)]))
+    specs += [rng.standard_normal(m).astype(np.float32) for m in (1000, 2048, 2049, 16385)]
+    while len(specs) < n:
+        specs.append(rng.standard_normal(int(rng.integers(2049, Lmax + 1))).astype(np.float32))
+    lens = np.array([x.size for x in specs], dtype=np.int32)
+    stride = Lmax + 1
+    scores = np.full((n, stride), np.nan, dtype=np.float32)
+    for i, r in enumerate(specs):
+        scores[i, : lens[i]] = r
+    gp.say(f"[gpu] top-k of {n} rows up to {Lmax} keys (three rows per CU)")
+    dev_scores = torch.from_numpy(scores).to(gp.DEV)
+    kv_start = torch.zeros(n, dtype=torch.int32, device=gp.DEV)
+    kv_len = torch.from_numpy(lens).to(gp.DEV)
+    idx, sc = ds.topk_select(dev_scores, kv_start, kv_len, Lmax, k, Lmax, want_score=True)
+    torch.cuda.synchronize()
+    got, got_sc = idx.cpu().numpy(), sc.cpu().numpy()
+    for i in range(n):
+        row = scores[i, : lens[i]]
+        want = np.sort(sa.topk_positions(row, k))
+        if want.size < k:
+            want = np.concatenate([want, np.full(k - want.size, -1)])
+        assert np.array_equal(got[i], want), f"row {i}: {np.setxor1d(got[i], want).size} differences"
+        m = min(k, int(lens[i]))
+        want_sc = row[want[:m]] + np.float32(0.0)  # -0.0 is reported as +0.0
+        assert np.array_equal(got_sc[i][:m], want_sc), f"row {i}: scores differ"
+
+
 def test_topk_rows_longer_than_the_cache():
     # rows longer than the 32768-key LDS cache: the threshold bucket is
     # compacted into the cache after the first radix pass when it fits, and
