@@ -347,10 +347,10 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
 //   n_seg*k candidates, which are in position order; padding scores are
 //   -inf, below every finite score (a key scored -inf is an unmapped one,
 //   whose row is -1 like a padding entry's, so ties there change nothing).
-// kMode 3: kMode 0 for launches of many long rows (512 threads, three
-//   workgroups per CU): the bitmap path reads the row twice from memory
-//   instead of caching it in LDS, and the general path works on a small
-//   block cache.
+// kMode 3: kMode 0 for launches of many rows of more than 4096 keys (512
+//   threads, three workgroups per CU): the bitmap path reads the row twice
+//   from memory instead of caching it in LDS, and the general path works on
+//   a small block cache.
 template <int kTkThreads, int kMode>
 __device__ __forceinline__ void topk_body(const TopkArgs& a, int32_t cache_keys) {
   constexpr int kTkWaves = kTkThreads / kWave;
@@ -717,10 +717,10 @@ ds_status launch_topk(const TopkArgs& a, hipStream_t s) {
   }
   const int32_t cache_keys = a.max_kv_len < kTkCacheKeys ? a.max_kv_len : kTkCacheKeys;
   const size_t smem = sizeof(uint32_t) * static_cast<size_t>(cache_keys > 0 ? cache_keys : 1);
-  if (a.max_kv_len > 16384 && a.max_kv_len <= kTkBitmapMaxLen && a.n_q >= 2 * device_cu_count()) {
-    // many long rows: three rows per CU, the memory passes of one under the
-    // LDS and ALU work of the others; a small block cache for the rare rows
-    // that leave the bitmap path
+  if (a.max_kv_len > 4096 && a.max_kv_len <= kTkBitmapMaxLen && a.n_q >= 2 * device_cu_count()) {
+    // many rows of more than 4096 keys: three rows per CU, the memory passes
+    // of one under the LDS and ALU work of the others; a small block cache
+    // for the rare rows that leave the bitmap path
     const int32_t ck = a.max_kv_len < kTkSmallCacheKeys ? a.max_kv_len : kTkSmallCacheKeys;
     topk_rows_kernel<<<a.n_q, 512, sizeof(uint32_t) * ck, s>>>(a, ck);
   } else if (a.max_kv_len > 16384) {
