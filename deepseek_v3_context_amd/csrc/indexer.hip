@@ -142,12 +142,13 @@ __device__ __forceinline__ float head_sum(const f32x16 (&acc)[kIxRowBlocks],
 // LDS with global_load_lds_dwordx4 (no VGPRs), double-buffered so that the
 // gather of the next tile overlaps the MFMAs of the current one; every wave
 // reads the shared tile's B fragments from LDS.  Two waves per SIMD.
-constexpr int kIxPWaves = 8;
+constexpr int kIxPWaves = 8;                       // waves (queries) per workgroup
 constexpr int kIxPHalf = 64;                       // keys per MFMA pass (two 32-key blocks)
+constexpr int kIxTileFp8 = 256, kIxTileBf16 = 128; // keys per tile
 template <bool kFp8>
 struct IxTile {
-  // keys per tile: 256 fp8 rows or 128 bf16 rows (about 36 KB of LDS)
-  static constexpr int kTile = kFp8 ? 256 : 128;
+  // keys per tile (256 fp8 rows or 128 bf16 rows: about 36 KB of LDS)
+  static constexpr int kTile = kFp8 ? kIxTileFp8 : kIxTileBf16;
   static constexpr int kRowBytes = kFp8 ? kIxDim : 2 * kIxDim;   // 128 / 256
   static constexpr int kRowShift = kFp8 ? 7 : 8;
   static constexpr int kLdsRow = kRowBytes + 16;                  // padded
@@ -509,6 +510,7 @@ indexer_paged_mfma_kernel(IndexerArgs a) {
 // [W*b/G, W*(b+1)/G) of the total weight W.
 constexpr int32_t kIxBWin = 2048;    // keys per score window
 constexpr int kIxBMaxQb = 1024;      // query blocks per launch
+constexpr int kIxBPerCu = 1;         // resident workgroups per CU
 
 template <bool kFp8>
 __device__ __forceinline__ void ix_window(int32_t lo, int32_t len, int64_t w, int64_t& tfirst,
@@ -564,7 +566,6 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
                 "windows hold whole tiles and whole fp8 scale blocks");
   static_assert(kIxPHalf <= kFp8BlockRows && kFp8BlockRows % kIxPHalf == 0,
                 "a 64-key half has one fp8 scale");
-  static_assert(2 * kWave * kIxPWaves >= kIxBMaxQb, "two query blocks per thread in the set-up");
   __shared__ float sc[kIxPWaves][kIxBWin];                  // scores of the current window
   __shared__ int32_t qb_lo[kIxBMaxQb], qb_len[kIxBMaxQb];   // union range of each block
   __shared__ int64_t wave_tot[2][kIxPWaves];
@@ -575,27 +576,30 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- set-up: ranges, tiles and weights of blocks 2*tid and 2*tid + 1.
-  // The launch's query ranges are staged in LDS first (in the score
-  // buffer, free until the walk) with coalesced loads, all in flight.
-  int64_t ql[16], qh[16];
+  // ---- set-up: ranges, tiles and weights of this thread's kBPT blocks
+  // (kBPT*tid ...).  The launch's query ranges are staged in LDS first (in
+  // the tile buffers, free until the walk) with coalesced loads, all in
+  // flight.
+  constexpr int kBPT = kIxBMaxQb / (kWave * kIxPWaves);   // query blocks per thread
+  constexpr int kQPT = kBPT * kIxPWaves;                    // their queries
+  static_assert(kBPT * kWave * kIxPWaves == kIxBMaxQb, "whole blocks per thread");
+  static_assert(sizeof(int32_t) * kIxBMaxQb * kIxPWaves <= kIxBufBytes, "the ranges fit a tile buffer");
+  int64_t ql[kQPT], qh[kQPT];
   {
-    constexpr int kPer = kIxBMaxQb * kIxPWaves / (kWave * kIxPWaves);
-    static_assert(2 * kIxBMaxQb * kIxPWaves <= kIxPWaves * kIxBWin, "the ranges fit the score buffer");
-    int32_t* s_start = reinterpret_cast<int32_t*>(&sc[0][0]);
-    int32_t* s_len = s_start + kIxBMaxQb * kIxPWaves;
+    int32_t* s_start = reinterpret_cast<int32_t*>(g_ix_buf0);
+    int32_t* s_len = reinterpret_cast<int32_t*>(g_ix_buf1);
     const int32_t j0 = qb0 * kIxPWaves;
     const int32_t nj = a.n_q - j0 < n_qb * kIxPWaves ? a.n_q - j0 : n_qb * kIxPWaves;
-    int32_t vs[kPer], vl[kPer];
+    int32_t vs[kQPT], vl[kQPT];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < kQPT; ++u) {
       const int32_t i = u * kWave * kIxPWaves + tid;
       const int32_t ic = i < nj ? i : nj - 1;
       vs[u] = a.kv_start[j0 + ic];
       vl[u] = a.kv_len[j0 + ic];
     }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < kQPT; ++u) {
       const int32_t i = u * kWave * kIxPWaves + tid;
       if (i < nj) {
         s_start[i] = vs[u];
@@ -604,9 +608,9 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int32_t q = 2 * tid + i / 8;
-      const int32_t jl = q * kIxPWaves + i % 8;
+    for (int i = 0; i < kQPT; ++i) {
+      const int32_t q = kBPT * tid + i / kIxPWaves;
+      const int32_t jl = q * kIxPWaves + i % kIxPWaves;
       const bool in = q < n_qb && jl < nj;
       const int32_t st = in ? s_start[jl] : 0, ln = in ? s_len[jl] : 0;
       const int64_t lo = st < 0 ? 0 : st;
@@ -617,12 +621,12 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
       qh[i] = ok ? hi : 0;
     }
   }
-  int64_t nt[2], wt[2];
+  int64_t nt[kBPT], wt[kBPT], sum_w = 0, sum_t = 0;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kBPT; ++k) {
     int64_t lo = INT64_MAX, hi = 0;
 #pragma unroll
-    for (int i = 8 * k; i < 8 * k + 8; ++i) {
+    for (int i = kIxPWaves * k; i < kIxPWaves * (k + 1); ++i) {
       if (qh[i] > ql[i]) {
         lo = ql[i] < lo ? ql[i] : lo;
         hi = qh[i] > hi ? qh[i] : hi;
@@ -632,14 +636,16 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
     const int32_t l32 = hi > lo ? static_cast<int32_t>(lo) : 0;
     nt[k] = ix_block_tiles<kFp8>(l32, len);
     wt[k] = nt[k] > 0 ? kIxBTileW * nt[k] + kIxBBlockW : 0;
-    const int32_t q = 2 * tid + k;
+    sum_w += wt[k];
+    sum_t += nt[k];
+    const int32_t q = kBPT * tid + k;
     if (q < n_qb) {
       qb_lo[q] = l32;
       qb_len[q] = len;
     }
   }
-  const int64_t incl_w = wave_incl_scan(wt[0] + wt[1], lane);
-  const int64_t incl_t = wave_incl_scan(nt[0] + nt[1], lane);
+  const int64_t incl_w = wave_incl_scan(sum_w, lane);
+  const int64_t incl_t = wave_incl_scan(sum_t, lane);
   if (lane == kWave - 1) {
     wave_tot[0][wave] = incl_w;
     wave_tot[1][wave] = incl_t;
@@ -657,18 +663,21 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
   const int64_t w_total = lane_value(sw, 0), t_total = lane_value(stt, 0);
   if (w_total == 0) return;
   // weight and tile prefixes of this thread's blocks
-  int64_t pw[2], pt[2];
-  pw[0] = bw + incl_w - wt[0] - wt[1];
-  pw[1] = pw[0] + wt[0];
-  pt[0] = bt + incl_t - nt[0] - nt[1];
-  pt[1] = pt[0] + nt[0];
+  int64_t pw[kBPT], pt[kBPT];
+  pw[0] = bw + incl_w - sum_w;
+  pt[0] = bt + incl_t - sum_t;
+#pragma unroll
+  for (int k = 1; k < kBPT; ++k) {
+    pw[k] = pw[k - 1] + wt[k - 1];
+    pt[k] = pt[k - 1] + nt[k - 1];
+  }
   const int64_t g0 = w_total * blockIdx.x / gridDim.x;
   const int64_t g1 = w_total * (blockIdx.x + 1) / gridDim.x;
   // tile i of a block starts at weight pw + kIxBBlockW + i * kIxBTileW and
   // belongs to the share its start falls in: count the tiles starting
   // before g0 and before g1
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kBPT; ++k) {
     auto before = [&](int64_t g) {
       int64_t c = g - pw[k] - kIxBBlockW;
       c = c <= 0 ? 0 : ceil_div(c, kIxBTileW);
@@ -683,14 +692,14 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
   if (f1 <= f0) return;   // the whole workgroup: no barrier below is skipped by part of it
   // the block holding tile f0 (the share's first), and its queries' ranges
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kBPT; ++k) {
     if (nt[k] > 0 && pt[k] <= f0 && f0 < pt[k] + nt[k]) {
-      first_qb = 2 * tid + k;
+      first_qb = kBPT * tid + k;
       first_off = static_cast<int32_t>(f0 - pt[k]);
 #pragma unroll
       for (int i = 0; i < kIxPWaves; ++i) {
-        first_lo[i] = ql[8 * k + i];
-        first_hi[i] = qh[8 * k + i];
+        first_lo[i] = ql[kIxPWaves * k + i];
+        first_hi[i] = qh[kIxPWaves * k + i];
       }
     }
   }
@@ -944,7 +953,7 @@ ds_status launch_indexer_scores(const IndexerArgs& a, hipStream_t s) {
   // one workgroup per CU, each an equal share of the key tiles of up to
   // kIxBMaxQb query blocks per launch
   const int32_t n_qblocks = static_cast<int32_t>(ceil_div(a.n_q, kIxPWaves));
-  const unsigned grid = static_cast<unsigned>(device_cu_count());
+  const unsigned grid = static_cast<unsigned>(device_cu_count() * kIxBPerCu);
   for (int32_t qb0 = 0; qb0 < n_qblocks; qb0 += kIxBMaxQb) {
     const int32_t n = n_qblocks - qb0 < kIxBMaxQb ? n_qblocks - qb0 : kIxBMaxQb;
     if (fp8)
