@@ -724,10 +724,11 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
     if ((p.w + 1) * kIxBWin < static_cast<int64_t>(lo) + len) {
       ++p.w;
     } else {
-      // next block with work (there is one: the share has tiles left)
+      // next block with work (there is one: the share has tiles left; the
+      // bound keeps the walk inside the launch's blocks regardless)
       do {
         ++p.qb;
-      } while (block_len(p.qb) == 0);
+      } while (p.qb + 1 < n_qb && block_len(p.qb) == 0);
       p.w = block_lo(p.qb) / kIxBWin;
     }
     enter_window(p);
@@ -740,7 +741,9 @@ indexer_prefill_balanced_kernel(IndexerArgs a, int32_t qb0, int32_t n_qb) {
   enter_window(cur);
   {
     int32_t off = __builtin_amdgcn_readfirstlane(first_off);
-    while (off >= cur.n_t) {
+    // (every window of a block with work has at least one tile; the second
+    // condition only bounds the loop)
+    while (off >= cur.n_t && cur.n_t > 0) {
       off -= cur.n_t;
       ++cur.w;
       enter_window(cur);
