@@ -90,14 +90,22 @@ gemm_nt_kernel(GemmArgs g, int32_t tiles_m, int32_t tiles_n, int32_t k_per_split
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
 
-  // workgroup -> (batch, split, tile): consecutive logical ids share an A
-  // row block (N tiles vary fastest) and run on one XCD, whose L2 then
-  // serves that block to all of them
+  // workgroup -> (batch, split, tile): consecutive logical ids run on one
+  // XCD and walk the tiles in groups of kGroupM row blocks, the row block
+  // varying fastest, so that the XCD's concurrent tiles (about 32) span a
+  // few A row blocks and a few B column blocks, which its L2 then serves to
+  // all of them (o_proj on 8192 tokens: 1905 -> 1790-1800 us against
+  // N tiles varying fastest)
   int64_t id = (gridDim.x & 7u) == 0 ? xcd_contiguous_id(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int32_t tn = static_cast<int32_t>(id % tiles_n);
-  id /= tiles_n;
-  const int32_t tm = static_cast<int32_t>(id % tiles_m);
-  id /= tiles_m;
+  constexpr int32_t kGroupM = 8;
+  const int64_t per_bs = static_cast<int64_t>(tiles_m) * tiles_n;
+  const int32_t t_in = static_cast<int32_t>(id % per_bs);
+  id /= per_bs;
+  const int32_t first_m = (t_in / (kGroupM * tiles_n)) * kGroupM;
+  const int32_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int32_t in_group = t_in - first_m * tiles_n;
+  const int32_t tm = first_m + in_group % gm;
+  const int32_t tn = in_group / gm;
   const int32_t split = static_cast<int32_t>(id % g.splits);
   const int32_t b = static_cast<int32_t>(id / g.splits);
   const int32_t m0 = tm * BM, n0 = tn * BN;
