@@ -506,8 +506,7 @@ indexer_paged_mfma_kernel(IndexerArgs a) {
 // Set-up: every workgroup stages the launch's query ranges in LDS
 // (coalesced loads, all in flight), computes each query block's range and
 // tile count, scans the weights and tile counts, and takes the tiles that
-// start in its share
-// [W*b/G, W*(b+1)/G) of the total weight W.
+// start in its share [W*b/G, W*(b+1)/G) of the total weight W.
 constexpr int32_t kIxBWin = 2048;    // keys per score window
 constexpr int kIxBMaxQb = 1024;      // query blocks per launch
 constexpr int kIxBPerCu = 1;         // resident workgroups per CU
