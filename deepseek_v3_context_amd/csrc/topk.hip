@@ -309,7 +309,9 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
     __syncthreads();
   }
 
-  // ---- ascending positions of the selected keys, mapped to rows
+  // ---- ascending positions of the selected keys (exactly k of them),
+  // ranked by one block scan into LDS (the candidate keys are consumed),
+  // then mapped to rows and written out with coalesced stores
   uint32_t sw[kWpt], c = 0;
 #pragma unroll
   for (int q = 0; q < kWpt; ++q) {
@@ -319,19 +321,22 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
   }
   uint32_t total;
   uint32_t slot = tk_block_scan<kTkWaves>(c, lane, wave, wave_tot, total);
+  uint32_t* sel = cand_key;
 #pragma unroll
   for (int q = 0; q < kWpt; ++q) {
     uint32_t x = sw[q];
     while (x) {
       const int e = __builtin_ctz(x);
       x &= x - 1u;
-      const int32_t pos = ((kWpt * tid + q) << 5) + e;
-      if (slot < k) {
-        out_idx[slot] = static_cast<int32_t>(topk_key_row(a, req, kv0 + pos));
-        if (out_score) out_score[slot] = order_key_to_float(float_order_key(row_scores[pos]));
-      }
+      if (slot < k) sel[slot] = static_cast<uint32_t>(((kWpt * tid + q) << 5) + e);
       ++slot;
     }
+  }
+  __syncthreads();
+  for (int32_t i = tid; i < static_cast<int32_t>(k); i += kTkThreads) {
+    const int32_t pos = static_cast<int32_t>(sel[i]);
+    out_idx[i] = static_cast<int32_t>(topk_key_row(a, req, kv0 + pos));
+    if (out_score) out_score[i] = order_key_to_float(float_order_key(row_scores[pos]));
   }
   return true;
 }
