@@ -467,8 +467,15 @@ def projections(wl, torch, ds, n, steps):
         ms = ev0.elapsed_time(ev1) / steps
         flops = 2.0 * n * N * K * batch
         tf = flops / (ms * 1e-3) / 1e12
+        # algorithmic HBM bytes: A, B and C once each (bf16); below the
+        # ridge (peak FLOP/s over peak bytes/s) the product is HBM-bound
+        nbytes = 2.0 * (n * K + N * K + n * N) * batch
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        hbm = flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
         out[name] = {"M": n, "N": N, "K": K, "batch": batch, "avg_us": round(ms * 1e3, 2),
-                     "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "tflops": round(tf, 1), "gbs": round(gbs, 1), "bytes": int(nbytes),
+                     "bound": "hbm" if hbm else "mfma",
+                     "frac": round(gbs / PEAK_HBM_GBS if hbm else tf / PEAK_BF16_TFLOPS, 4),
                      "splits": 1 if need == 0 else need // (4 * n * N * batch)}
         del a, w, c, ws
     torch.cuda.empty_cache()

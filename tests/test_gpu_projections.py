@@ -106,9 +106,11 @@ def test_absorbed_products_on_strided_views():
     assert (np.abs(_f64(o.cpu()).reshape(n, H, DV) - ref_o) <= bound).all()
 
 
-@pytest.mark.parametrize("name", ["o_proj", "indexer_w_k", "mla_q_up"])
+@pytest.mark.parametrize("name", ["o_proj", "indexer_w_k", "mla_q_up", "mla_q_down"])
 def test_full_size_sampled_rows(name):
-    # the 65536-token prefill's 8192 rank tokens; 24 sampled rows, all columns
+    # the 65536-token prefill's 8192 rank tokens; 24 sampled rows, all
+    # columns.  Tile widths: 256 (o_proj, q_up), 128 with split-K (w_k), 128
+    # chosen so that no split is needed (q_down: 192 wide tiles < the CUs)
     N, K = SHAPES[name]
     M = 8192
     g = torch.Generator(device=gp.DEV).manual_seed(5)
