@@ -136,6 +136,17 @@ _add(replace(WORKLOADS["small_prefill_3req_cp4"], name="small_prefill_sharp",
 _add(Workload("tiny_prefill_bf16", "prefill", seed=22, seqlens=(300, 5, 90),
               cp_size=3, cp_rank=0, topk=64,
               description="tiny multi-request bf16 at full model dims"))
+_add(Workload("small_prefill_topk777", "prefill", seed=23, seqlens=(2600, 900),
+              cp_size=4, cp_rank=1, topk=777,
+              description="two requests, cp 4, rank 1; top-k 777, not a"
+                          " multiple of the 32-row MLA tile: a partial last"
+                          " tile, and rows that select every causal key next"
+                          " to rows that select a strict subset; bf16"))
+_add(Workload("small_decode_topk333_fp8", "decode", seed=24, n_req=7, len_lo=40,
+              len_hi=4000, topk=333, page_size=64, kv_fmt="fp8",
+              description="7 requests, lengths in [40, 4000], top-k 333 (the"
+                          " decode splits end off the tile grid); latent KV and"
+                          " indexer keys e4m3fn"))
 
 
 def get(name: str) -> Workload:

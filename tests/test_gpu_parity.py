@@ -112,7 +112,7 @@ def _check_rows(wl, g, orc_sel, rows, inp, kv_data, kv_scale):
 
 PREFILL_SMALL = ["tiny_prefill_t256_cp4", "tiny_prefill_dense", "tiny_prefill_bf16",
                  "small_prefill_3req_cp4", "small_prefill_3req_cp4_fp8",
-                 "small_prefill_topk2048", "small_prefill_sharp"]
+                 "small_prefill_topk2048", "small_prefill_sharp", "small_prefill_topk777"]
 PREFILL_FULL = ["prefill_t8000_cp8", "prefill_6req_t25305_cp8", "prefill_t65536_cp8_fp8"]
 
 
@@ -181,6 +181,10 @@ def test_decode_small_all_rows():
 
 def test_decode_small_fp8_all_rows():
     _check_decode("small_decode_paged_fp8", all_rows=True)
+
+
+def test_decode_small_fp8_topk_off_the_tile_grid():
+    _check_decode("small_decode_topk333_fp8", all_rows=True)
 
 
 def test_decode_full_size_all_requests():
