@@ -142,6 +142,14 @@ _add(Workload("small_prefill_topk777", "prefill", seed=23, seqlens=(2600, 900),
                           " multiple of the 32-row MLA tile: a partial last"
                           " tile, and rows that select every causal key next"
                           " to rows that select a strict subset; bf16"))
+_add(Workload("small_prefill_cp1", "prefill", seed=25, seqlens=(700, 300),
+              cp_size=1, cp_rank=0, topk=256,
+              description="no context parallelism (cp 1): the split and the"
+                          " rerange are the identity; two requests; bf16"))
+_add(Workload("small_prefill_cp16", "prefill", seed=26, seqlens=(1000, 37, 5),
+              cp_size=16, cp_rank=15, topk=256,
+              description="cp 16, last rank: a 37-token request leaves the rank"
+                          " two tokens, a 5-token one none; bf16"))
 _add(Workload("small_decode_topk333_fp8", "decode", seed=24, n_req=7, len_lo=40,
               len_hi=4000, topk=333, page_size=64, kv_fmt="fp8",
               description="7 requests, lengths in [40, 4000], top-k 333 (the"

@@ -112,7 +112,8 @@ def _check_rows(wl, g, orc_sel, rows, inp, kv_data, kv_scale):
 
 PREFILL_SMALL = ["tiny_prefill_t256_cp4", "tiny_prefill_dense", "tiny_prefill_bf16",
                  "small_prefill_3req_cp4", "small_prefill_3req_cp4_fp8",
-                 "small_prefill_topk2048", "small_prefill_sharp", "small_prefill_topk777"]
+                 "small_prefill_topk2048", "small_prefill_sharp", "small_prefill_topk777",
+                 "small_prefill_cp1", "small_prefill_cp16"]
 PREFILL_FULL = ["prefill_t8000_cp8", "prefill_6req_t25305_cp8", "prefill_t65536_cp8_fp8"]
 
 
