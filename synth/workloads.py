@@ -150,6 +150,15 @@ _add(Workload("small_prefill_cp16", "prefill", seed=26, seqlens=(1000, 37, 5),
               cp_size=16, cp_rank=15, topk=256,
               description="cp 16, last rank: a 37-token request leaves the rank"
                           " two tokens, a 5-token one none; bf16"))
+_add(Workload("small_decode_splits", "decode", seed=27, n_req=4, len_lo=40,
+              len_hi=3000, topk=2048, page_size=64,
+              description="4 requests, lengths in [40, 3000], top-k 2048: the"
+                          " MLA splits each query's 2048 slots 8 ways, and the"
+                          " splits past a short context hold only -1 (empty"
+                          " partials for the combine); bf16"))
+_add(Workload("small_decode_splits_fp8", "decode", seed=28, n_req=4, len_lo=40,
+              len_hi=3000, topk=2048, page_size=64, kv_fmt="fp8",
+              description="as above with e4m3fn latent KV and indexer keys"))
 _add(Workload("small_decode_topk333_fp8", "decode", seed=24, n_req=7, len_lo=40,
               len_hi=4000, topk=333, page_size=64, kv_fmt="fp8",
               description="7 requests, lengths in [40, 4000], top-k 333 (the"

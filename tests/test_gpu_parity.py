@@ -188,6 +188,11 @@ def test_decode_small_fp8_topk_off_the_tile_grid():
     _check_decode("small_decode_topk333_fp8", all_rows=True)
 
 
+@pytest.mark.parametrize("name", ["small_decode_splits", "small_decode_splits_fp8"])
+def test_decode_split_partials_with_empty_splits(name):
+    _check_decode(name, all_rows=True)
+
+
 def test_decode_full_size_all_requests():
     _check_decode("decode_32req_paged", all_rows=True)
 
