@@ -422,10 +422,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 //
 // Softmax reference: the logits of a head are taken relative to its
 // maximum over the first tile and never rescaled afterwards (so the
-// accumulators are only ever touched by MFMA).  A later tile whose maximum
-// exceeds the reference by more than 2^kWideBail (weights up to 2^64 are
-// exact in fp32/bf16 range terms) makes the workgroup start over with the
-// exact maximum from a first pass over all its rows.
+// accumulators are only ever touched by MFMA).  A later tile in which a
+// head's weight 2^(logit - reference) could exceed 2^kWideBail (weights up
+// to 2^64 are exact in fp32/bf16 range terms) makes the workgroup start
+// over with the exact maximum from a first pass over all its rows.  The
+// lagged (128-head) loop tests the head's weight sum over the tile, which
+// it forms anyway, instead of the tile's maximum; the sum bounds every
+// weight, and a large sum of moderate weights only costs an exact restart.
 constexpr float kWideBail = 64.f;
 // QK steps before the end of a tile's QK at which the lagged loop issues the
 // LDS reads of the PV products that follow (their latency then overlaps the
@@ -807,7 +810,11 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
     // h0 + 16hb; v = 8hb + 4kb + i.
     auto micro = [&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
-      if constexpr (u < 2) {                       // raw maximum of head block u
+      if constexpr (u < 4 && !kFirst) {
+        // after the first tile the maximum is not needed: a rise past the
+        // reference shows in the head's weight sum (unit 55), for fewer
+        // vector instructions between the products
+      } else if constexpr (u < 2) {                       // raw maximum of head block u
         const float m0 = max3_raw(st[0][u][0], st[0][u][1], st[0][u][2]);
         const float m1 = max3_raw(st[0][u][3], st[1][u][0], st[1][u][1]);
         mx[u] = max3_raw(m0, m1, max_raw(st[1][u][2], st[1][u][3]));
@@ -832,7 +839,7 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
           nm[hb] = -m_ref[hb];
         }
       } else if constexpr (u == 5) {
-        beyond = !exact && ((mx[0] > m_ref[0] + kWideBail) || (mx[1] > m_ref[1] + kWideBail));
+        if constexpr (kFirst) beyond = false;   // the reference is this tile's maximum
       } else if constexpr (u < 6 + 3 * 16) {       // weights exp2(scale2 * s - m_ref), three steps per value
         constexpr int v = (u - 6) / 3, ph = (u - 6) % 3;
         constexpr int hb = v >> 3, kb = (v >> 2) & 1, i = v & 3;
@@ -859,7 +866,13 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
         for (int hb = 0; hb < 2; ++hb) {
           const auto b2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(psum[hb]),
                                                             __float_as_uint(psum[hb]), false, false);
-          l_run[hb] += __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+          const float tile_sum = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+          l_run[hb] += tile_sum;
+          // a weight above 2^kWideBail (or an infinite one) puts the head's
+          // tile sum above it; a sum above it without such a weight only
+          // costs a restart, which is exact
+          static_assert(kWideBail == 64.f, "the bound below is 2^kWideBail");
+          if constexpr (!kFirst) beyond = beyond || (!exact && !(tile_sum <= 0x1p64f));
         }
       } else if constexpr (u == 56) {
 #pragma unroll
