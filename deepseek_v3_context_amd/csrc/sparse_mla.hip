@@ -773,16 +773,21 @@ mla_bf16_wide_kernel(MlaArgs a, int32_t keys_per_split) {
   constexpr int kCBL = kCB < 8 ? kCB : 8;   // column blocks whose V fragments are held
   bf16x8 vf[kCBL];
   bf16x8 pf[3];
+  // P^T fragment reads of the tile's PV products: this lane's address in the
+  // parity buffer being read is formed once per tile (by pv_reads); head
+  // group hg adds 256 bytes, an instruction offset
+  const __attribute__((address_space(3))) uint8_t* p_rd = nullptr;
   auto load_p = [&](int pb, int hg) __attribute__((always_inline)) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    return __builtin_bit_cast(bf16x8, sh.p[pb][ln >> 4][hg * 16 + (ln & 15)]);
+    (void)pb;   // p_rd already points into parity buffer pb
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(p_rd + hg * 256));
   };
   // the LDS reads the PV products of a tile start with: its V^T fragments
   // (transposed reads of the tile in vtile) and P^T of head groups 0 and 1
   auto pv_reads = [&](const uint8_t* vtile, int pb) __attribute__((always_inline)) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    p_rd = (const __attribute__((address_space(3))) uint8_t*)(&sh.p[pb][ln >> 4][ln & 15]);
     const int voff = wide_voff(ln, wave * kCols);
 #pragma unroll
     for (int c = 0; c < kCBL; ++c) {
