@@ -41,16 +41,57 @@ constexpr int kTkBins = 4096;
 constexpr int kTkCandMax = 2048;
 constexpr int32_t kTkBitmapMaxLen = kTopkOnePassMaxLen;
 
+// Physical KV row of logical position l (kv_start + key position) of
+// request req, or -1.  Positions and kv_start are int32 by interface, so
+// 0 <= l < 2^32 and the page division is an exact 32-bit one (a 64-bit
+// division is a long instruction sequence).
 __device__ __forceinline__ int64_t topk_key_row(const TopkArgs& a, int32_t req,
                                                 int64_t l) {
   if (l < 0) return -1;
   if (a.page_table == nullptr) return l < a.k_rows ? l : -1;
-  const int64_t ps = a.page_size;
-  const int64_t pg = l / ps;
-  if (req < 0 || req >= a.n_req || pg >= a.max_pages) return -1;
+  const uint32_t ps = static_cast<uint32_t>(a.page_size);
+  const uint32_t pg = static_cast<uint32_t>(l) / ps;
+  if (req < 0 || req >= a.n_req || pg >= static_cast<uint32_t>(a.max_pages)) return -1;
   const int32_t pid = a.page_table[static_cast<int64_t>(req) * a.max_pages + pg];
-  const int64_t row = static_cast<int64_t>(pid) * ps + (l - pg * ps);
+  const int64_t row = static_cast<int64_t>(pid) * ps + (static_cast<uint32_t>(l) - pg * ps);
   return (pid >= 0 && row < a.k_rows) ? row : -1;
+}
+
+// topk_key_row of kN positions kv0 + pos[i] at once, every page-table load
+// issued before any is used; entries with use[i] false come out as -1.
+template <int kN>
+__device__ __forceinline__ void topk_key_rows(const TopkArgs& a, int32_t req, int64_t kv0,
+                                              const int32_t (&pos)[kN], const bool (&use)[kN],
+                                              int32_t (&row)[kN]) {
+  if (a.page_table == nullptr) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int64_t l = kv0 + pos[i];
+      row[i] = use[i] && l >= 0 && l < a.k_rows ? static_cast<int32_t>(l) : -1;
+    }
+    return;
+  }
+  const bool req_ok = req >= 0 && req < a.n_req;
+  const int32_t* tab = a.page_table + static_cast<int64_t>(req_ok ? req : 0) * a.max_pages;
+  const uint32_t ps = static_cast<uint32_t>(a.page_size);
+  uint32_t pg[kN];
+  int32_t pid[kN];
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    const int64_t l = kv0 + pos[i];
+    pg[i] = l >= 0 ? static_cast<uint32_t>(l) / ps : 0xffffffffu;
+  }
+#pragma unroll
+  for (int i = 0; i < kN; ++i)
+    pid[i] = tab[use[i] && pg[i] < static_cast<uint32_t>(a.max_pages) ? pg[i] : 0u];
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    const int64_t l = kv0 + pos[i];
+    const int64_t r = static_cast<int64_t>(pid[i]) * ps + (static_cast<uint32_t>(l) - pg[i] * ps);
+    const bool ok = use[i] && req_ok && pg[i] < static_cast<uint32_t>(a.max_pages) &&
+                    pid[i] >= 0 && r < a.k_rows;
+    row[i] = ok ? static_cast<int32_t>(r) : -1;
+  }
 }
 
 // Exclusive prefix sum of one count per thread over the workgroup, in
@@ -333,10 +374,27 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
     }
   }
   __syncthreads();
-  for (int32_t i = tid; i < static_cast<int32_t>(k); i += kTkThreads) {
-    const int32_t pos = static_cast<int32_t>(sel[i]);
-    out_idx[i] = static_cast<int32_t>(topk_key_row(a, req, kv0 + pos));
-    if (out_score) out_score[i] = order_key_to_float(float_order_key(row_scores[pos]));
+  // every slot of the thread at once: page-table and score loads in flight
+  // together
+  constexpr int kOut = kTopkMax / kTkThreads;
+  int32_t pos[kOut], row[kOut];
+  bool use[kOut];
+  float sc[kOut];
+#pragma unroll
+  for (int q = 0; q < kOut; ++q) {
+    const uint32_t i = static_cast<uint32_t>(tid + q * kTkThreads);
+    use[q] = i < k;
+    pos[q] = use[q] ? static_cast<int32_t>(sel[i]) : 0;
+  }
+  topk_key_rows<kOut>(a, req, kv0, pos, use, row);
+#pragma unroll
+  for (int q = 0; q < kOut; ++q) sc[q] = out_score && use[q] ? row_scores[pos[q]] : 0.f;
+#pragma unroll
+  for (int q = 0; q < kOut; ++q) {
+    if (!use[q]) continue;
+    const int32_t i = tid + q * kTkThreads;
+    out_idx[i] = row[q];
+    if (out_score) out_score[i] = order_key_to_float(float_order_key(sc[q]));
   }
   return true;
 }
