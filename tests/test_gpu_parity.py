@@ -406,6 +406,19 @@ def test_integer_outputs_repeatable():
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
 
 
+@pytest.mark.parametrize("name", ["small_decode_paged", "small_decode_splits_fp8"])
+def test_decode_outputs_repeatable(name):
+    # split partials merged by the combine kernel, fp8 and bf16 pools: the
+    # same inputs give the same selection and bit-identical outputs
+    wl = get(name)
+    inp = draw_decode(wl)
+    a = gp.run_decode(wl, inp, want_scores=False)
+    b = gp.run_decode(wl, inp, want_scores=False)
+    for key in ("topk_idx", "topk_score", "out", "lse"):
+        assert np.array_equal(a[key].view(np.uint32) if a[key].dtype == np.float32 else a[key],
+                              b[key].view(np.uint32) if b[key].dtype == np.float32 else b[key]), key
+
+
 @pytest.mark.parametrize("heads", [32, 64])
 def test_mla_head_counts_below_128(heads):
     # the ABI takes any head count that is a multiple of 32 (up to 128): the
