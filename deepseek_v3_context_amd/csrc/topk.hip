@@ -126,7 +126,7 @@ __device__ __forceinline__ uint32_t tk_block_scan(uint32_t v, int lane, int wave
 template <int kTkThreads, bool kCached>
 __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_scores,
                             int32_t* out_idx, float* out_score, int32_t req, int64_t kv0,
-                            uint32_t* cache, uint32_t* hw, uint16_t* cand_pos,
+                            uint32_t* cache, int32_t c16_len, uint32_t* hw, uint16_t* cand_pos,
                             uint32_t* cand_key, uint32_t* wave_tot, uint32_t& sh_digit,
                             uint32_t& sh_remaining, uint32_t& sh_count, uint32_t& sh_ncand) {
   constexpr int kTkWaves = kTkThreads / kWave;
@@ -189,7 +189,7 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
       uint32_t key[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) key[e] = float_order_key(f[e]);
-      if constexpr (kCached) {
+      if (kCached || t + 4 <= c16_len) {
         if (t + 4 <= L) {
           *reinterpret_cast<uint2*>(c16 + t) =
               make_uint2((key[0] >> 16) | (key[1] & 0xffff0000u), (key[2] >> 16) | (key[3] & 0xffff0000u));
@@ -223,8 +223,9 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
     uint32_t bits = 0, tbits = 0;
     if (w < n_words) {
       const int32_t p0 = w << 5;
-      if constexpr (!kCached) {
-        // the row again from memory (L2 or HBM): 32 keys per word
+      if (!kCached && p0 + 32 > c16_len) {
+        // words past the row's cached head, again from memory (L2 or
+        // HBM): 32 keys per word
         float4 v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -412,13 +413,14 @@ __device__ bool bitmap_path(const TopkArgs& a, int32_t L, const float* row_score
 //   whose row is -1 like a padding entry's, so ties there change nothing).
 // kMode 3: kMode 0 for launches of many rows of more than 4096 keys (512
 //   threads, three workgroups per CU): the bitmap path reads the row twice
-//   from memory instead of caching it in LDS, and the general path works on
-//   a small block cache.
+//   from memory, except its first keys, whose top 16 bits stay in the small
+//   block cache between the two passes; the general path works on that
+//   block cache.
 template <int kTkThreads, int kMode>
 __device__ __forceinline__ void topk_body(const TopkArgs& a, int32_t cache_keys) {
   constexpr int kTkWaves = kTkThreads / kWave;
   // the bitmap path: with the row's top 16 bits cached in LDS (kMode 0,
-  // 1024 threads), or reading the row twice from memory (kMode 3: 512
+  // 1024 threads), or reading all but its head twice from memory (kMode 3: 512
   // threads and a small LDS footprint, so that three workgroups share a CU
   // and one's memory passes run under the others' LDS and ALU work)
   constexpr bool kBitmap = (kMode == 0 && kTkThreads == 1024) || kMode == 3;
@@ -514,7 +516,9 @@ __device__ __forceinline__ void topk_body(const TopkArgs& a, int32_t cache_keys)
   if constexpr (kBitmap) {
     if ((kMode == 3 || L <= 2 * cache_keys) && L <= kTkBitmapMaxLen &&
         bitmap_path<kTkThreads, kMode == 0>(a, L, row_scores, out_idx,
-        out_score, req, kv0, cache, hist_words, cand_pos, reinterpret_cast<uint32_t*>(sel_t),
+        out_score, req, kv0, cache,
+        kMode == 0 ? L : (L < 2 * cache_keys ? L : 2 * cache_keys) & ~31,
+        hist_words, cand_pos, reinterpret_cast<uint32_t*>(sel_t),
         wave_tot, sh_digit, sh_remaining, sh_count, sh_ncand)) {
       return;
     }
