@@ -31,7 +31,7 @@ namespace ds32cp {
 
 constexpr int kTkPer = 8;                 // consecutive keys per thread and step
 constexpr int32_t kTkCacheKeys = 32768;   // 128 KiB of LDS
-constexpr int32_t kTkSmallCacheKeys = 4096;   // 16 KiB: three workgroups per CU (kMode 3)
+constexpr int32_t kTkSmallCacheKeys = 6144;   // 24 KiB: with 28 KiB of static LDS, three workgroups per CU (kMode 3)
 // Bitmap path: bins of the first digit (the top 12 bits of the 32-bit
 // key), the most threshold-bucket keys it resolves in LDS, and the longest
 // row it takes (16-bit keys in the cache; positions fit in 16 bits).  Only
